@@ -1,0 +1,418 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check compares the oracle with an independent source of truth: 40-digit
+decimal brute force on tiny inputs, closed forms, invariants of the
+definition, library dtype conversions, and the element counts printed on the
+ctyun.cn FlashAttention article (section "MAC分析").  ``test_planted_mistakes``
+plants plausible mistakes into a copy of the oracle's row computation and
+shows that at least one pin fails for each.
+"""
+
+import decimal
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as oatt
+from oracle.tiled import q_outer_traffic_elements
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = decimal.Decimal
+
+
+# ----------------------------------------------------------------- decoders
+
+def test_decode_bf16_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = oracle.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def test_decode_f16_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.decode_f16(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def test_decode_f32_sampled_patterns():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0, 0x80000000, 1, 0x807FFFFF, 0x00800000, 0x7F7FFFFF,
+                         0x7F800000, 0xFF800000, 0x7FC00000, 0x3F800000],
+                        dtype=np.uint32)
+    bits = np.concatenate([bits, specials])
+    with np.errstate(invalid="ignore"):
+        ref = bits.view(np.float32).astype(np.float64)
+    got = oracle.decode_f32(bits)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+
+
+# ------------------------------------------------------- decimal brute force
+
+def brute_attention(q, k, v, scale, prec=40):
+    """Attention by its definition in 40-digit decimal arithmetic, with no max
+    subtraction and plain left-to-right sums.  q, k: (N, d); v: (N, dv)."""
+    ctx = decimal.Context(prec=prec)
+    n, d = q.shape
+    dv = v.shape[1]
+    sc = D(float(scale))
+    o = np.empty((n, dv))
+    lse = np.empty(n)
+    for i in range(n):
+        e = []
+        for j in range(n):
+            acc = D(0)
+            for c in range(d):
+                acc = ctx.add(acc, ctx.multiply(D(float(q[i, c])), D(float(k[j, c]))))
+            e.append(ctx.exp(ctx.multiply(sc, acc)))
+        l = D(0)
+        for x in e:
+            l = ctx.add(l, x)
+        for c in range(dv):
+            acc = D(0)
+            for j in range(n):
+                acc = ctx.add(acc, ctx.multiply(ctx.divide(e[j], l), D(float(v[j, c]))))
+            o[i, c] = float(acc)
+        lse[i] = float(ctx.ln(l))
+    return o, lse
+
+
+def brute_softmax(x, prec=40):
+    ctx = decimal.Context(prec=prec)
+    e = [D(0) if xi == -np.inf else ctx.exp(D(float(xi))) for xi in x]
+    l = D(0)
+    for t in e:
+        l = ctx.add(l, t)
+    return np.array([float(ctx.divide(t, l)) for t in e]), l
+
+
+def _tiny_case(seed, n, d, dv=None, spread=1.0):
+    rng = np.random.default_rng(seed)
+    dv = d if dv is None else dv
+    q = rng.normal(size=(n, d)) * spread
+    k = rng.normal(size=(n, d)) * spread
+    v = rng.normal(size=(n, dv))
+    return q, k, v
+
+
+def _oracle_one_head(q, k, v, scale):
+    o, lse = oracle.standard_attention(q[None, None], k[None, None], v[None, None], scale)
+    return o[0, 0], lse[0, 0]
+
+
+def brute_force_pin_holds(attention_fn, cases):
+    """True iff ``attention_fn`` agrees with decimal brute force on ``cases``."""
+    for seed, n, d, dv, spread, scale in cases:
+        q, k, v = _tiny_case(seed, n, d, dv, spread)
+        o, lse = attention_fn(q, k, v, scale)
+        ob, lb = brute_attention(q, k, v, scale)
+        if not (np.allclose(o, ob, rtol=1e-13, atol=1e-13)
+                and np.allclose(lse, lb, rtol=1e-13, atol=1e-13)):
+            return False
+    return True
+
+
+BRUTE_CASES = [
+    (1, 1, 1, 1, 1.0, 1.0),
+    (2, 2, 3, 2, 1.0, 0.5),
+    (3, 3, 3, 3, 1.5, 0.7),     # N == d == dv: a transposed operand still runs
+    (4, 5, 4, 3, 1.0, 0.5),
+    (5, 8, 8, 8, 2.0, 1.0 / math.sqrt(8)),
+    (6, 16, 8, 4, 1.0, 1.0 / math.sqrt(8)),
+    (7, 16, 2, 5, 3.0, 0.9),    # wide score spread: max subtraction matters in fp64
+]
+
+
+def test_brute_force_tiny():
+    assert brute_force_pin_holds(_oracle_one_head, BRUTE_CASES)
+
+
+def test_rows_variant_matches_brute_force():
+    q, k, v = _tiny_case(11, 13, 4, 3)
+    rows = [0, 5, 12]
+    o, lse = oracle.standard_attention_rows(q[None, None], k[None, None], v[None, None], 0.6, rows)
+    ob, lb = brute_attention(q, k, v, 0.6)
+    np.testing.assert_allclose(o[0, 0], ob[rows], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], lb[rows], rtol=1e-13, atol=1e-13)
+
+
+# -------------------------------------------------------------- closed forms
+
+def closed_form_pin_holds(attention_fn):
+    """Hand-derived cases of the definition."""
+    ok = True
+    # two keys, one query: scores (0, s); p = (1, e^s) / (1 + e^s)
+    for s in (0.0, 1.0, -2.5, 30.0):
+        a, b = 0.25, -3.0
+        q = np.array([[1.0]])
+        k = np.array([[0.0], [1.0]])
+        v = np.array([[a], [b]])
+        o, lse = attention_fn(q[[0, 0]], k, v, s)
+        o_ref = (a + b * math.exp(s)) / (1.0 + math.exp(s))
+        lse_ref = math.log1p(math.exp(s)) if s < 20 else s + math.log1p(math.exp(-s))
+        ok &= abs(o[0, 0] - o_ref) <= 1e-14 * max(1.0, abs(o_ref))
+        ok &= abs(lse[0] - lse_ref) <= 1e-14 * max(1.0, abs(lse_ref))
+    # N = 1: O = V exactly, LSE = scale * q.k
+    q, k, v = _tiny_case(21, 1, 6, 4)
+    o, lse = attention_fn(q, k, v, 0.3)
+    ok &= bool(np.array_equal(o, v))
+    ok &= abs(lse[0] - 0.3 * float(q[0] @ k[0])) <= 1e-14 * max(1.0, abs(lse[0]))
+    # Q = 0: every score is 0, so O_i = mean_j V_j and LSE = ln N
+    _, k, v = _tiny_case(22, 9, 4, 3)
+    o, lse = attention_fn(np.zeros((9, 4)), k, v, 1.0)
+    ok &= bool(np.allclose(o, v.mean(axis=0)[None, :], rtol=0, atol=1e-14))
+    ok &= bool(np.allclose(lse, math.log(9), rtol=0, atol=1e-14))
+    # asymmetric 2x2 with d=2 and V = I (so O = P): catches a transposed
+    # score matrix or a softmax taken down columns
+    q = np.array([[2.0, 0.0], [0.0, 3.0]])
+    k = np.array([[1.0, 0.0], [0.0, 0.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o, lse = attention_fn(q, k, v, 1.0)
+    # row 0: scores (2, 0) -> p = (e^2, 1)/(e^2+1); row 1: scores (0, 0) -> p = (1/2, 1/2)
+    e2 = math.exp(2.0)
+    ok &= bool(np.allclose(o[0], [e2 / (e2 + 1), 1 / (e2 + 1)], rtol=0, atol=1e-14))
+    ok &= bool(np.allclose(o[1], [0.5, 0.5], rtol=0, atol=1e-14))
+    ok &= abs(lse[0] - math.log(e2 + 1)) <= 1e-14 and abs(lse[1] - math.log(2)) <= 1e-14
+    return bool(ok)
+
+
+def test_closed_forms():
+    assert closed_form_pin_holds(_oracle_one_head)
+
+
+def test_identity_values_give_p_rows_summing_to_one():
+    # V = I makes O = P: entries in [0, 1], rows sum to 1; V = ones gives O = 1.
+    for seed, n, d in [(31, 7, 3), (32, 40, 16)]:
+        q, k, _ = _tiny_case(seed, n, d, spread=2.0)
+        p, _ = _oracle_one_head(q, k, np.eye(n), 0.5)
+        assert (p >= 0).all() and (p <= 1).all()
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+        ones, _ = _oracle_one_head(q, k, np.ones((n, 5)), 0.5)
+        np.testing.assert_allclose(ones, 1.0, rtol=0, atol=1e-13)
+
+
+def test_shift_invariance():
+    # K' = K + 1 u^T shifts row i's scores by scale * q_i . u: O is unchanged
+    # and LSE_i moves by exactly that amount.  Values on a 1/8 grid.
+    rng = np.random.default_rng(41)
+    q = rng.integers(-32, 33, size=(2, 3, 50, 16)) / 8.0
+    k = rng.integers(-32, 33, size=(2, 3, 50, 16)) / 8.0
+    v = rng.normal(size=(2, 3, 50, 16))
+    u = rng.integers(-32, 33, size=16) / 8.0
+    scale = 0.25
+    o1, l1 = oracle.standard_attention(q, k, v, scale)
+    o2, l2 = oracle.standard_attention(q, k + u, v, scale)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, scale * (q @ u), rtol=0, atol=1e-11)
+
+
+def test_permutation_equivariance():
+    rng = np.random.default_rng(42)
+    q, k, v = (rng.normal(size=(1, 2, 33, 8)) for _ in range(3))
+    o, lse = oracle.standard_attention(q, k, v, 0.4)
+    pk = rng.permutation(33)
+    o2, lse2 = oracle.standard_attention(q, k[:, :, pk], v[:, :, pk], 0.4)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+    pq = rng.permutation(33)
+    o3, lse3 = oracle.standard_attention(q[:, :, pq], k, v, 0.4)
+    np.testing.assert_allclose(o3, o[:, :, pq], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse3, lse[:, :, pq], rtol=0, atol=1e-13)
+
+
+def test_dominant_key_selects_its_value():
+    rng = np.random.default_rng(43)
+    q, k, v = _tiny_case(44, 12, 8)
+    j = 7
+    k[j] = 60.0 * q[3] / np.linalg.norm(q[3])
+    o, _ = _oracle_one_head(q, k, v, 1.0)
+    np.testing.assert_allclose(o[3], v[j], rtol=0, atol=1e-12)
+
+
+def test_batches_and_heads_are_independent():
+    rng = np.random.default_rng(45)
+    q, k, v = (rng.normal(size=(2, 3, 10, 4)) for _ in range(3))
+    o, lse = oracle.standard_attention(q, k, v, 0.5)
+    for b in range(2):
+        for h in range(3):
+            ob, lb = brute_attention(q[b, h], k[b, h], v[b, h], 0.5)
+            np.testing.assert_allclose(o[b, h], ob, rtol=1e-13, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], lb, rtol=1e-13, atol=1e-13)
+
+
+def test_row_chunking_does_not_change_rows():
+    rng = np.random.default_rng(46)
+    q, k, v = (rng.normal(size=(1, 1, 37, 4)) for _ in range(3))
+    o1, l1 = oracle.standard_attention(q, k, v, 0.5, row_chunk=1024)
+    o2, l2 = oracle.standard_attention(q, k, v, 0.5, row_chunk=5)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-15)
+
+
+# ----------------------------------------- blockwise merge / online recurrence
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 16, 32])
+def test_two_block_merge_equals_softmax(n):
+    rng = np.random.default_rng(100 + n)
+    for spread in (1.0, 30.0):
+        x = rng.normal(size=n) * spread
+        ref, l_ref = brute_softmax(x)
+        m_ref = x.max()
+        for k in range(0, n + 1):
+            s, m, l, f = oracle.two_block_softmax(x, k)
+            np.testing.assert_allclose(s, ref, rtol=0, atol=1e-14)
+            assert m == m_ref
+            # l(x) = sum e^{x - m(x)}; f_global = e^{x - m(x)}
+            ctx = decimal.Context(prec=40)
+            l_dec = float(ctx.divide(l_ref, ctx.exp(D(float(m_ref)))))
+            assert abs(l - l_dec) <= 1e-14 * l_dec
+            np.testing.assert_allclose(f / l, ref, rtol=0, atol=1e-14)
+
+
+def test_two_block_merge_with_masked_block():
+    x = np.array([-np.inf, -np.inf, 0.5, 2.0, -1.0])
+    for k in range(6):
+        s, _, _, _ = oracle.two_block_softmax(x, k)
+        ref, _ = brute_softmax(x)
+        np.testing.assert_allclose(s, ref, rtol=0, atol=1e-15)
+        assert s[0] == 0.0 and s[1] == 0.0
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 33])
+def test_online_recurrence_equals_weighted_average(n):
+    rng = np.random.default_rng(200 + n)
+    for spread in (1.0, 25.0):
+        s = rng.normal(size=n) * spread
+        v = rng.normal(size=(n, 3))
+        p, l_ref = brute_softmax(s)
+        ctx = decimal.Context(prec=40)
+        o_ref = np.array([float(sum((D(float(p[j])) * D(float(v[j, c])) for j in range(n)), D(0)))
+                          for c in range(3)])
+        for block in sorted({1, 2, 3, n, n + 4}):
+            o, m, l = oracle.online_softmax_output(s, v, block=block)
+            np.testing.assert_allclose(o, o_ref, rtol=1e-13, atol=1e-14)
+            assert m == s.max()
+            l_dec = float(ctx.divide(l_ref, ctx.exp(D(float(s.max())))))
+            assert abs(l - l_dec) <= 1e-13 * l_dec
+
+
+def test_online_recurrence_masked_prefix():
+    # a leading block of -inf scores exercises the -inf guard
+    s = np.array([-np.inf, -np.inf, -np.inf, 1.0, 3.0])
+    v = np.arange(10, dtype=float).reshape(5, 2)
+    for block in (1, 2, 3):
+        o, m, l = oracle.online_softmax_output(s, v, block=block)
+        w = np.array([math.exp(-2.0), 1.0]) / (1.0 + math.exp(-2.0))
+        np.testing.assert_allclose(o, w @ v[3:], rtol=0, atol=1e-14)
+        assert m == 3.0 and np.isfinite(l)
+
+
+# ------------------------------------------------------------ tiled mirror
+
+@pytest.mark.parametrize("order", ["q_outer", "kv_outer"])
+@pytest.mark.parametrize("br,bc", [(1, 1), (4, 3), (7, 16), (64, 5), (100, 100)])
+def test_tiled_equals_definition(order, br, bc):
+    rng = np.random.default_rng(300 + br * 7 + bc)
+    q = rng.normal(size=(2, 2, 37, 8)) * 2.0
+    k = rng.normal(size=(2, 2, 37, 8)) * 2.0
+    v = rng.normal(size=(2, 2, 37, 5))
+    o_ref, l_ref = oracle.standard_attention(q, k, v, 0.7)
+    o, lse, cnt = oracle.tiled_online_attention(q, k, v, 0.7, br, bc, order=order)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
+    n, d, dv, heads = 37, 8, 5, 4
+    if order == "q_outer":
+        total = cnt["Q"] + cnt["K"] + cnt["V"] + cnt["O"] + cnt["LSE"]
+        # K is d wide, V is dv wide
+        want = heads * (n * d + n * d * math.ceil(n / br) + n * dv * math.ceil(n / br)
+                        + n * dv + n)
+        assert total == want
+        assert q_outer_traffic_elements(n, d, d, br) == n * d + 2 * n * d * math.ceil(n / br) + n * d + n
+    else:
+        # the dominant term of the ctyun.cn article's "FA MAC分析": Q read T_c times
+        assert cnt["Q"] == heads * n * d * math.ceil(n / bc)
+        assert cnt["K"] == heads * n * d and cnt["V"] == heads * n * dv
+
+
+# -------------------------------------------------------------- MAC count
+
+def _eval(expr, N, d):
+    return eval(expr, {"__builtins__": {}}, {"N": N, "d": d})
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (5, 3), (16, 8), (33, 4)])
+def test_mac_count_matches_printed_formulas(N, d):
+    with open(os.path.join(GOLDEN, "mac_standard_attention.json"), encoding="utf-8") as fh:
+        g = json.load(fh)
+    rng = np.random.default_rng(N * 100 + d)
+    q, k, v = (rng.normal(size=(N, d)) for _ in range(3))
+    o, per_line = oracle.standard_attention_mac(q, k, v, 0.5)
+    for (reads, writes), spec in zip(per_line, g["per_line"]):
+        assert reads == sum(_eval(e, N, d) for e in spec["reads"].values())
+        assert writes == sum(_eval(e, N, d) for e in spec["writes"].values())
+        assert reads + writes == _eval(spec["printed_total"], N, d)
+    assert sum(r + w for r, w in per_line) == _eval(g["printed_sum"], N, d)
+    transfers = sum(len(s["reads"]) + len(s["writes"]) for s in g["per_line"])
+    assert transfers == g["matrix_transfers"]
+    o_ref, _ = _oracle_one_head(q, k, v, 0.5)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------- planted mistakes
+
+def _mutant(kind):
+    def rows(qh, kh, vh, scale):
+        s = scale * (qh @ kh.T)
+        if kind == "no_scale":
+            s = qh @ kh.T
+        if kind == "transposed_scores":
+            s = scale * (kh @ qh.T)
+        m = s.max(axis=1, keepdims=True)
+        f = np.exp(s - m)
+        if kind == "sign":
+            f = np.exp(m - s)
+        l = f.sum(axis=1, keepdims=True)
+        if kind == "column_sum":
+            l = f.sum(axis=0, keepdims=True)
+        p = f / l
+        o = p @ vh
+        if kind == "transposed_p":
+            o = p.T @ vh
+        if kind == "dropped_term":
+            o = p[:, 1:] @ vh[1:]
+        lse = (m + np.log(l))[:, 0] if kind != "lse_no_max" else np.log(l)[:, 0]
+        if kind == "column_sum":
+            lse = (m + np.log(l[:, :1]))[:, 0]
+        return o, lse
+    return rows
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "transposed_scores", "sign", "column_sum",
+                                  "transposed_p", "dropped_term", "lse_no_max"])
+def test_planted_mistakes_fail_a_pin(kind, monkeypatch):
+    monkeypatch.setattr(oatt, "_rows_of_head", _mutant(kind))
+    cases = [c for c in BRUTE_CASES if c[1] == c[2] == c[3]] + [BRUTE_CASES[3]]
+
+    def guarded(fn):
+        try:
+            return fn()
+        except (ValueError, IndexError):
+            return False     # a shape error is a failed pin too
+    held = guarded(lambda: brute_force_pin_holds(_oracle_one_head, cases)) and \
+        guarded(lambda: closed_form_pin_holds(_oracle_one_head))
+    assert not held, f"mutant {kind!r} passed every pin"

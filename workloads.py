@@ -1,0 +1,83 @@
+"""Seeded synthetic attention workloads shared by tests and bench.py.
+
+This module only draws random tensors and names the five workloads; it holds
+none of the attention arithmetic, so both the HIP path's callers and the
+oracle's callers can use it without sharing any of the method.
+
+Recipe: every tensor is drawn on the CPU in fp32 from its own
+``torch.Generator`` seeded with ``seed_base + {0, 1, 2}`` for Q, K, V, then
+rounded once to the target dtype (round-to-nearest-even), so the GPU and the
+oracle see bit-identical values.  The five named workloads use
+``seed_base = 1000 * index``.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+# Distributions:
+#   "normal": Q, K, V i.i.d. N(0, 1)
+#   "stress": Q, K i.i.d. N(0, 4^2) so scaled scores have std 16 (span about
+#             +-60 at d=128) and the running row maximum keeps moving late in
+#             the key sweep; V ~ U(-1, 1)
+WORKLOADS = {
+    1: dict(name="single-head fp32 B1 H1 N256 d64", B=1, H=1, N=256, d=64,
+            dtype="fp32", dist="normal"),
+    2: dict(name="bf16 B4 H16 N1024 d64", B=4, H=16, N=1024, d=64,
+            dtype="bf16", dist="normal"),
+    3: dict(name="bf16 B2 H16 N4096 d128", B=2, H=16, N=4096, d=128,
+            dtype="bf16", dist="normal"),
+    4: dict(name="long-sequence bf16 B1 H32 N16384 d128", B=1, H=32, N=16384,
+            d=128, dtype="bf16", dist="normal"),
+    5: dict(name="numerics-stress fp16 B2 H8 N8191 d128", B=2, H=8, N=8191,
+            d=128, dtype="fp16", dist="stress"),
+}
+
+HEADLINE = 3
+
+
+def default_scale(d):
+    """1/sqrt(d) evaluated in fp64 and rounded once to fp32; the same fp32
+    value is handed to the GPU and (widened) to the oracle."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def make_qkv(B, H, N, d, dtype="bf16", seed_base=0, dist="normal"):
+    """Return CPU tensors q, k, v of shape (B, H, N, d) in ``dtype``."""
+    shape = (B, H, N, d)
+    out = []
+    for i in range(3):
+        g = torch.Generator().manual_seed(seed_base + i)
+        if dist == "normal":
+            t = torch.randn(shape, generator=g, dtype=torch.float32)
+        elif dist == "stress":
+            if i < 2:
+                t = 4.0 * torch.randn(shape, generator=g, dtype=torch.float32)
+            else:
+                t = 2.0 * torch.rand(shape, generator=g, dtype=torch.float32) - 1.0
+        else:
+            raise ValueError(f"unknown distribution {dist!r}")
+        out.append(t.to(DTYPES[dtype]).contiguous())
+    return tuple(out)
+
+
+def workload_qkv(index):
+    """Inputs of named workload ``index`` (1..5): (q, k, v, scale, spec)."""
+    spec = WORKLOADS[index]
+    q, k, v = make_qkv(spec["B"], spec["H"], spec["N"], spec["d"],
+                       spec["dtype"], 1000 * index, spec["dist"])
+    return q, k, v, default_scale(spec["d"]), spec
+
+
+def raw_bits(t):
+    """Bit patterns of a CPU tensor as a numpy unsigned array (uint16 for
+    16-bit dtypes, uint32 for fp32)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    raise TypeError(f"unsupported dtype {t.dtype}")
