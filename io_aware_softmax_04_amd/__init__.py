@@ -1,0 +1,188 @@
+"""Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
+
+The functions ``fa_fwd``, ``fa_naive_fwd``, ``fa_naive_workspace_bytes``,
+``fa_status_string``, ``fa_last_error`` and ``fa_version`` carry the names
+and meaning of the entry points declared in ``include/fa_api.h``; they only
+marshal torch tensors into pointers, sizes and the current HIP stream.  Every
+step of the computation runs in the HIP kernels of ``libiofa.so``; there is
+no CPU fallback, and a missing library raises instead of computing.
+
+``forward`` and ``naive_forward`` are conveniences that allocate the outputs
+(and the naive path's workspaces) with torch and call the entry points.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
+    "fa_fwd", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
+    "fa_last_error", "fa_version", "forward", "naive_forward", "default_scale",
+]
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libiofa.so")
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{fa_status_string(status)} (status {status}): {detail}")
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libiofa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built: run `python -m io_aware_softmax_04_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, fp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, ctypes.c_float,
+                           ctypes.c_int, vp]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_naive_fwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, i64, i64, i64, i64,
+                                 ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_naive_fwd.restype = ctypes.c_int
+    lib.fa_naive_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.fa_naive_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------- marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _fptr(t):
+    return None if t is None else ctypes.cast(ctypes.c_void_p(t.data_ptr()),
+                                              ctypes.POINTER(ctypes.c_float))
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _shape(q, k, v, o):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be (B, H, N, d), got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check(status):
+    if status != 0:
+        raise FaError(status, fa_last_error())
+
+
+# --------------------------------------------------------- entry points
+
+def fa_fwd(q, k, v, o, lse, scale, stream=None):
+    """Fused forward; writes o (B, H, N, d) and lse (B, H, N) fp32 in place."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, N)):
+        raise ValueError("lse must be a contiguous fp32 (B, H, N) tensor")
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), B, H, N, d,
+                        float(scale), _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+def fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream=None):
+    """Naive three-kernel forward; s_ws and p_ws are byte (uint8) tensors of
+    fa_naive_workspace_bytes() bytes each; lse may be None."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o)
+    need = fa_naive_workspace_bytes(B, H, N, q.dtype)
+    for name, ws in (("s_ws", s_ws), ("p_ws", p_ws)):
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"{name} holds fewer than {need} bytes")
+    with torch.cuda.device(q.device):
+        st = lib.fa_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(s_ws),
+                              _ptr(p_ws), B, H, N, d, float(scale), _DTYPE_CODE[q.dtype],
+                              _stream(stream, q.device))
+    _check(st)
+
+
+def fa_naive_workspace_bytes(B, H, N, dtype):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_naive_workspace_bytes(B, H, N, code))
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_last_error():
+    return load_library().fa_last_error().decode()
+
+
+def fa_version():
+    return int(load_library().fa_version())
+
+
+# ---------------------------------------------------------- conveniences
+
+def default_scale(d):
+    """1/sqrt(d) in fp64 rounded once to fp32."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def forward(q, k, v, scale=None, stream=None):
+    """Allocate O and LSE and run the fused forward.  Returns (o, lse)."""
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, stream)
+    return o, lse
+
+
+def naive_forward(q, k, v, scale=None, want_lse=True, stream=None):
+    """Allocate O, LSE and both workspaces and run the naive three-kernel
+    path.  Returns (o, lse or None)."""
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if want_lse else None
+    nbytes = max(fa_naive_workspace_bytes(B, H, N, q.dtype), 16)
+    s_ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    p_ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream)
+    return o, lse

@@ -1,0 +1,168 @@
+// C ABI of the gfx950 exact-attention library: argument validation, error
+// reporting and dispatch to the kernel launchers.  Validation touches no HIP
+// API, so a call with bad arguments returns its status on any host, with or
+// without a GPU.
+#include "../../include/fa_api.h"
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "fa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case FA_F32: return 4;
+    case FA_F16: return 2;
+    case FA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t round_up8(int64_t n) { return (n + 7) / 8 * 8; }
+
+struct Region {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+// Shared checks of fa_fwd and fa_naive_fwd.  Returns FA_OK and sets *empty
+// when there is nothing to do.
+int check_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 bool lse_required, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 int dtype, bool* empty) {
+  *empty = false;
+  if (elem_bytes(dtype) == 0)
+    return fail(FA_ERR_DTYPE, "dtype " + std::to_string(dtype) + " is not FA_F32, FA_F16 or FA_BF16");
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_SHAPE, "B, H and N must be >= 0 (got B=" + std::to_string(B) +
+                                  " H=" + std::to_string(H) + " N=" + std::to_string(N) + ")");
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_HEAD_DIM, "head dimension d must be 64 or 128 (got " + std::to_string(d) + ")");
+  if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX)
+    return fail(FA_ERR_SHAPE, "B * H must be < 2^31");
+  if (N * d >= (int64_t(1) << 31)) return fail(FA_ERR_SHAPE, "N * d must be < 2^31");
+  if (B * H * N >= (int64_t(1) << 31)) return fail(FA_ERR_SHAPE, "B * H * N must be < 2^31");
+  if (!Q || !K || !V || !O) return fail(FA_ERR_NULL, "Q, K, V and O must not be NULL");
+  if (lse_required && !LSE) return fail(FA_ERR_NULL, "LSE must not be NULL");
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+    return fail(FA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+  if (LSE && !aligned(LSE, 4)) return fail(FA_ERR_ALIGN, "LSE must be 4-byte aligned");
+  return FA_OK;
+}
+
+int check_aliasing(const Region* in, int nin, const Region* out, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(out[i].p, out[i].bytes, in[j].p, in[j].bytes))
+        return fail(FA_ERR_ALIAS, std::string(out[i].name) + " overlaps input " + in[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i].p, out[i].bytes, out[j].p, out[j].bytes))
+        return fail(FA_ERR_ALIAS, std::string(out[i].name) + " overlaps " + out[j].name);
+  }
+  return FA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FA_OK;
+  return fail(FA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+           int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  bool empty = false;
+  int st = check_common(Q, K, V, O, LSE, true, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  const size_t tensor = static_cast<size_t>(B * H * N * d) * elem_bytes(dtype);
+  const size_t lse = static_cast<size_t>(B * H * N) * sizeof(float);
+  const Region in[3] = {{Q, tensor, "Q"}, {K, tensor, "K"}, {V, tensor, "V"}};
+  const Region out[2] = {{O, tensor, "O"}, {LSE, lse, "LSE"}};
+  st = check_aliasing(in, 3, out, 2);
+  if (st != FA_OK) return st;
+  if (iofa::fused_workgroups(dtype, B * H, N) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_fused(a), "fused forward launch");
+}
+
+int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, void* S_ws,
+                 void* P_ws, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype,
+                 void* stream) {
+  g_last_error.clear();
+  bool empty = false;
+  int st = check_common(Q, K, V, O, LSE, false, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!S_ws || !P_ws) return fail(FA_ERR_NULL, "S_ws and P_ws must not be NULL");
+  if (!aligned(S_ws, 16) || !aligned(P_ws, 16))
+    return fail(FA_ERR_ALIGN, "S_ws and P_ws must be 16-byte aligned");
+  if (N > iofa::kNaiveMaxN)
+    return fail(FA_ERR_SHAPE, "the naive path supports N <= " + std::to_string(iofa::kNaiveMaxN));
+  const size_t tensor = static_cast<size_t>(B * H * N * d) * elem_bytes(dtype);
+  const size_t lse = LSE ? static_cast<size_t>(B * H * N) * sizeof(float) : 0;
+  const size_t ws = fa_naive_workspace_bytes(B, H, N, dtype);
+  const Region in[3] = {{Q, tensor, "Q"}, {K, tensor, "K"}, {V, tensor, "V"}};
+  const Region out[4] = {{O, tensor, "O"}, {LSE, lse, "LSE"}, {S_ws, ws, "S_ws"}, {P_ws, ws, "P_ws"}};
+  st = check_aliasing(in, 3, out, 4);
+  if (st != FA_OK) return st;
+  if (iofa::naive_max_workgroups(dtype, B * H, N) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::NaiveArgs a{{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)},
+                    S_ws, P_ws, round_up8(N)};
+  return hip_status(iofa::launch_naive(a), "naive forward launch");
+}
+
+size_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
+  const int e = elem_bytes(dtype);
+  if (e == 0 || B < 0 || H < 0 || N < 0) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N) *
+         static_cast<size_t>(round_up8(N)) * static_cast<size_t>(e);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension";
+    case FA_ERR_DTYPE: return "unsupported dtype";
+    case FA_ERR_ALIGN: return "misaligned pointer";
+    case FA_ERR_SCALE: return "non-finite scale";
+    case FA_ERR_ALIAS: return "overlapping buffers";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,392 @@
+// Naive three-kernel attention for gfx950: the standard-attention contrast
+// whose device-memory traffic section "MAC分析 / 标准Transformer MAC分析" of
+// the ctyun.cn FlashAttention article counts line by line:
+//   kernel 1: read Q, K; write S = scale * Q K^T        (2Nd + N^2 elements)
+//   kernel 2: read S; write P = softmax(S) row by row  (2N^2)
+//   kernel 3: read P, V; write O = P V                  (N^2 + 2Nd)
+// S and P are stored in the input element type with row stride ldS (N
+// rounded up to 8, so each row starts 16-byte aligned); kernel 2 writes
+// zeros into P's padding columns, so kernel 3 can read whole 8-key chunks.
+// The matrix products of 16-bit inputs use v_mfma_f32_32x32x16 with fp32
+// accumulation; fp32 inputs use plain fp32 FMAs.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace iofa {
+
+namespace {
+
+constexpr int kQRows = 128;        // query rows per workgroup (4 waves x 32)
+constexpr int kKeysPerWg = 256;    // keys per workgroup in kernel 1
+constexpr int kMaxChunks = 16;     // 8-element chunks per thread in kernel 2
+
+// ------------------------------------------------ element access (kernel 2)
+
+struct Ld16Bf16 {
+  __device__ static inline float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static inline uint16_t from_f32(float x) { return Bf16::bits(x); }
+  __device__ static inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+};
+struct Ld16F16 {
+  __device__ static inline float to_f32(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+  }
+  __device__ static inline uint16_t from_f32(float x) { return F16::bits(x); }
+  __device__ static inline float ex(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+};
+
+template <class E>
+__device__ inline void load8_16(const uint16_t* p, float* v) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = E::to_f32(half_of(w, e));
+}
+template <class E>
+__device__ inline void store8_16(uint16_t* p, const float* v) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack2(E::from_f32(v[2 * e]), E::from_f32(v[2 * e + 1]));
+  *reinterpret_cast<u32x4*>(p) = w;
+}
+
+__device__ inline float block_reduce(float x, bool is_max, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float y = __shfl_xor(x, off, 64);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+// ------------------------------------------------------- kernel 1 (16-bit)
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void naive_scores_16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    uint16_t* __restrict__ S, int N, int ldS, int qtiles, int ktiles, int num_wg,
+    float scale) {
+  constexpr int BC = 64, KS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = xcd_logical_id(blockIdx.x, num_wg);
+  const int bh = L / (qtiles * ktiles);
+  const int rem = L % (qtiles * ktiles);
+  const int qt = rem / ktiles, kt = rem % ktiles;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+
+  const int q = qt * kQRows + wave * 32 + l32;
+  typename T::vec8 qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = (q < N) ? gmem_vec8<T>(Q + head + static_cast<size_t>(q) * D + 16 * kk + 8 * hi)
+                     : __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
+  uint16_t* Srow = S + (static_cast<size_t>(bh) * N + q) * ldS;
+
+  for (int sub = 0; sub < kKeysPerWg / BC; ++sub) {
+    const int k0 = kt * kKeysPerWg + sub * BC;
+    if (k0 >= N) break;
+    RowTile<D, BC, KS> t;
+    t.load(K + head + static_cast<size_t>(k0) * D, N - k0, tid);
+    t.store(Ks, tid);
+    __syncthreads();
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+        s[sb] = T::mfma(lds_vec8<T>(Ks + (32 * sb + l32) * KS + 16 * kk + 8 * hi), qf[kk], s[sb]);
+    if (q < N) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int key = k0 + 32 * sb + 8 * g + 4 * hi;
+          uint16_t b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[i] = T::bits(s[sb][4 * g + i] * scale);
+          if (key + 3 < N) {
+            u32x2 w;
+            w[0] = pack2(b[0], b[1]);
+            w[1] = pack2(b[2], b[3]);
+            *reinterpret_cast<u32x2*>(Srow + key) = w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key + i < N) Srow[key + i] = b[i];
+          }
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------- kernel 2 (all)
+
+template <class E>
+__global__ __launch_bounds__(256) void naive_softmax_16(
+    const uint16_t* __restrict__ S, uint16_t* __restrict__ P, float* __restrict__ LSE,
+    int N, int ldS) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  const uint16_t* s = S + row * ldS;
+  uint16_t* p = P + row * ldS;
+  const int nch = ldS / 8;
+  float v[kMaxChunks][8];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      load8_16<E>(s + c * 8, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (c * 8 + e >= N) v[i][e] = -__builtin_inff();
+        mx = fmaxf(mx, v[i][e]);
+      }
+    }
+  }
+  mx = block_reduce(mx, true, red);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = E::ex(v[i][e] - mx);
+        sum += v[i][e];
+      }
+    }
+  }
+  sum = block_reduce(sum, false, red);
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      float w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = v[i][e] * inv;
+      store8_16<E>(p + c * 8, w);
+    }
+  }
+  if (LSE != nullptr && threadIdx.x == 0) LSE[row] = mx + logf(sum);
+}
+
+__global__ __launch_bounds__(256) void naive_softmax_f32(
+    const float* __restrict__ S, float* __restrict__ P, float* __restrict__ LSE, int N,
+    int ldS) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  const float* s = S + row * ldS;
+  float* p = P + row * ldS;
+  const int nch = ldS / 8;
+  float v[kMaxChunks][8];
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      const float4 a = *reinterpret_cast<const float4*>(s + c * 8);
+      const float4 b = *reinterpret_cast<const float4*>(s + c * 8 + 4);
+      v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
+      v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (c * 8 + e >= N) v[i][e] = -__builtin_inff();
+        mx = fmaxf(mx, v[i][e]);
+      }
+    }
+  }
+  mx = block_reduce(mx, true, red);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = expf(v[i][e] - mx);
+        sum += v[i][e];
+      }
+    }
+  }
+  sum = block_reduce(sum, false, red);
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nch) {
+      *reinterpret_cast<float4*>(p + c * 8) =
+          make_float4(v[i][0] / sum, v[i][1] / sum, v[i][2] / sum, v[i][3] / sum);
+      *reinterpret_cast<float4*>(p + c * 8 + 4) =
+          make_float4(v[i][4] / sum, v[i][5] / sum, v[i][6] / sum, v[i][7] / sum);
+    }
+  }
+  if (LSE != nullptr && threadIdx.x == 0) LSE[row] = mx + logf(sum);
+}
+
+// ------------------------------------------------------- kernel 3 (16-bit)
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void naive_pv_16(
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, int N, int ldS, int qtiles, int num_wg) {
+  constexpr int BC = 64, VS = BC + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int L = xcd_logical_id(blockIdx.x, num_wg);
+  const int bh = L / qtiles, qt = L % qtiles;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int q = qt * kQRows + wave * 32 + l32;
+  const uint16_t* Prow = P + (static_cast<size_t>(bh) * N + q) * ldS;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+
+  for (int k0 = 0; k0 < N; k0 += BC) {
+    VtTile<D, BC, VS, false> vt;
+    vt.load(V + head + static_cast<size_t>(k0) * D, N - k0, tid);
+    vt.store(Vt, tid);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kidx = k0 + 16 * ks + 8 * hi;
+      const auto pf = (q < N && kidx < ldS)
+                          ? gmem_vec8<T>(Prow + kidx)
+                          : __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+        o[cb] = T::mfma(lds_vec8<T>(Vt + (32 * cb + l32) * VS + 16 * ks + 8 * hi), pf, o[cb]);
+    }
+    __syncthreads();
+  }
+  if (q < N) {
+    uint16_t* Oq = O + head + static_cast<size_t>(q) * D;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack2(T::bits(o[cb][4 * g + 0]), T::bits(o[cb][4 * g + 1]));
+        w[1] = pack2(T::bits(o[cb][4 * g + 2]), T::bits(o[cb][4 * g + 3]));
+        *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * hi) = w;
+      }
+  }
+}
+
+// --------------------------------------------------- kernels 1, 3 (fp32)
+
+// One thread per score; 16 x 16 score tile per workgroup.
+__global__ __launch_bounds__(256) void naive_scores_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, float* __restrict__ S,
+    int N, int D, int ldS, int tiles, float scale) {
+  const int per_head = tiles * tiles;
+  const int bh = blockIdx.x / per_head, t = blockIdx.x % per_head;
+  const int i = (t / tiles) * 16 + threadIdx.x / 16;
+  const int j = (t % tiles) * 16 + threadIdx.x % 16;
+  if (i >= N || j >= N) return;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const float* qi = Q + head + static_cast<size_t>(i) * D;
+  const float* kj = K + head + static_cast<size_t>(j) * D;
+  float acc = 0.f;
+  for (int c = 0; c < D; ++c) acc = fmaf(qi[c], kj[c], acc);
+  S[(static_cast<size_t>(bh) * N + i) * ldS + j] = acc * scale;
+}
+
+// One thread per output element.
+__global__ __launch_bounds__(256) void naive_pv_f32(
+    const float* __restrict__ P, const float* __restrict__ V, float* __restrict__ O,
+    int N, int D, int ldS, int64_t total) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx % D);
+  const int64_t rowg = idx / D;  // bh * N + i
+  const int64_t bh = rowg / N;
+  const float* prow = P + rowg * ldS;
+  const float* vh = V + bh * N * D;
+  float acc = 0.f;
+  for (int j = 0; j < N; ++j) acc = fmaf(prow[j], vh[static_cast<size_t>(j) * D + c], acc);
+  O[idx] = acc;
+}
+
+// ---------------------------------------------------------------- launch
+
+template <class T, class E, int D>
+hipError_t launch_naive16(const NaiveArgs& a) {
+  const FwdArgs& f = a.f;
+  const int N = static_cast<int>(f.N), ldS = static_cast<int>(a.ldS);
+  const int qtiles = (N + kQRows - 1) / kQRows;
+  const int ktiles = (N + kKeysPerWg - 1) / kKeysPerWg;
+  const int wg1 = static_cast<int>(f.BH * qtiles * ktiles);
+  hipLaunchKernelGGL((naive_scores_16<T, D>), dim3(wg1), dim3(256), 0, f.stream,
+                     static_cast<const uint16_t*>(f.Q), static_cast<const uint16_t*>(f.K),
+                     static_cast<uint16_t*>(a.S), N, ldS, qtiles, ktiles, wg1, f.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((naive_softmax_16<E>), dim3(static_cast<unsigned>(f.BH * N)), dim3(256), 0,
+                     f.stream, static_cast<const uint16_t*>(a.S), static_cast<uint16_t*>(a.P),
+                     f.LSE, N, ldS);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int wg3 = static_cast<int>(f.BH * qtiles);
+  hipLaunchKernelGGL((naive_pv_16<T, D>), dim3(wg3), dim3(256), 0, f.stream,
+                     static_cast<const uint16_t*>(a.P), static_cast<const uint16_t*>(f.V),
+                     static_cast<uint16_t*>(f.O), N, ldS, qtiles, wg3);
+  return hipGetLastError();
+}
+
+hipError_t launch_naive32(const NaiveArgs& a) {
+  const FwdArgs& f = a.f;
+  const int N = static_cast<int>(f.N), D = static_cast<int>(f.d), ldS = static_cast<int>(a.ldS);
+  const int tiles = (N + 15) / 16;
+  hipLaunchKernelGGL(naive_scores_f32, dim3(static_cast<unsigned>(f.BH * tiles * tiles)), dim3(256),
+                     0, f.stream, static_cast<const float*>(f.Q), static_cast<const float*>(f.K),
+                     static_cast<float*>(a.S), N, D, ldS, tiles, f.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(naive_softmax_f32, dim3(static_cast<unsigned>(f.BH * N)), dim3(256), 0,
+                     f.stream, static_cast<const float*>(a.S), static_cast<float*>(a.P), f.LSE, N,
+                     ldS);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = f.BH * N * D;
+  hipLaunchKernelGGL(naive_pv_f32, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                     f.stream, static_cast<const float*>(a.P), static_cast<const float*>(f.V),
+                     static_cast<float*>(f.O), N, D, ldS, total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t naive_max_workgroups(int dtype, int64_t BH, int64_t N) {
+  if (dtype == kDtypeF32) {
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t a = BH * tiles * tiles, b = BH * N, c = (BH * N * 128 + 255) / 256;
+    return a > b ? (a > c ? a : c) : (b > c ? b : c);
+  }
+  const int64_t qt = (N + kQRows - 1) / kQRows, kt = (N + kKeysPerWg - 1) / kKeysPerWg;
+  const int64_t a = BH * qt * kt, b = BH * N;
+  return a > b ? a : b;
+}
+
+hipError_t launch_naive(const NaiveArgs& a) {
+  const int dt = a.f.dtype;
+  const bool d128 = a.f.d == 128;
+  if (dt == kDtypeBF16)
+    return d128 ? launch_naive16<Bf16, Ld16Bf16, 128>(a) : launch_naive16<Bf16, Ld16Bf16, 64>(a);
+  if (dt == kDtypeF16)
+    return d128 ? launch_naive16<F16, Ld16F16, 128>(a) : launch_naive16<F16, Ld16F16, 64>(a);
+  return launch_naive32(a);
+}
+
+}  // namespace iofa

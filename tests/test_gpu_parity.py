@@ -1,0 +1,231 @@
+"""GPU parity of the fused and the naive paths against the fp64 oracle,
+called through the C ABI (python binding -> libiofa.so)."""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_softmax_04_amd as iofa
+from helpers import TOL, assert_parity, errors, oracle_full, oracle_rows, sample_rows, widen
+from workloads import WORKLOADS, default_scale, make_qkv, workload_qkv
+
+pytestmark = pytest.mark.gpu
+
+DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    iofa.load_library()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(fn, q, k, v, scale, dev, **kw):
+    out = fn(q.to(dev), k.to(dev), v.to(dev), scale, **kw)
+    torch.cuda.synchronize()
+    o, lse = out
+    return o.cpu(), (lse.cpu() if lse is not None else None)
+
+
+# ------------------------------------------------------- named workloads
+
+FULL_ORACLE = {1, 2}          # small enough for the full fp64 oracle
+
+
+@pytest.mark.parametrize("idx", sorted(WORKLOADS))
+def test_fused_workload(idx, dev):
+    q, k, v, scale, spec = workload_qkv(idx)
+    _say(f"fused workload {idx}: {spec['name']} scale={scale}")
+    o, lse = _run(iofa.forward, q, k, v, scale, dev)
+    N = spec["N"]
+    if idx in FULL_ORACLE:
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+        res = assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"fused w{idx}")
+    else:
+        rows = sample_rows(N, seed=idx)
+        o_ref, lse_ref = oracle_rows(q, k, v, scale, rows)
+        res = assert_parity(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, q.dtype,
+                            f"fused w{idx} ({rows.size} sampled rows/head)")
+    _say(f"  max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
+
+
+# ------------------------------------------------------------ ragged shapes
+
+RAGGED_N = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_ragged(dtype, d, dev):
+    for N in RAGGED_N:
+        q, k, v = make_qkv(1, 3, N, d, dtype, seed_base=10 * N + d, dist="normal")
+        scale = default_scale(d)
+        _say(f"fused ragged {dtype} d={d} N={N}")
+        o, lse = _run(iofa.forward, q, k, v, scale, dev)
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+        assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"ragged {dtype} d={d} N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fused_stress_distribution_small(dtype, dev):
+    # scores spanning +-60 with a ragged tail, small enough for the full oracle
+    q, k, v = make_qkv(1, 2, 777, 128, dtype, seed_base=555, dist="stress")
+    scale = default_scale(128)
+    o, lse = _run(iofa.forward, q, k, v, scale, dev)
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"stress {dtype}")
+
+
+def test_fused_many_heads(dev):
+    # a grid of 4096 workgroups over short sequences; every head checked
+    q, k, v = make_qkv(8, 256, 130, 64, "bf16", seed_base=77)
+    scale = default_scale(64)
+    o, lse = _run(iofa.forward, q, k, v, scale, dev)
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o, lse, o_ref, lse_ref, q.dtype, "many heads")
+
+
+def test_fused_other_scales(dev):
+    q, k, v = make_qkv(1, 2, 300, 128, "bf16", seed_base=91)
+    for scale in (0.0, -0.125, 0.5):
+        o, lse = _run(iofa.forward, q, k, v, scale, dev)
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+        assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"scale={scale}")
+
+
+# ------------------------------------------------------ invariants on GPU
+
+def test_shift_invariance_on_gpu(dev):
+    # K and u on a 1/8 grid in [-4, 4], so K + 1 u^T is exact in bf16
+    g = torch.Generator().manual_seed(2024)
+    B, H, N, d = 1, 4, 2000, 128
+    q = (torch.randint(-32, 33, (B, H, N, d), generator=g) / 8.0).to(torch.bfloat16)
+    k = (torch.randint(-32, 33, (B, H, N, d), generator=g) / 8.0).to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    u = torch.randint(-32, 33, (d,), generator=g) / 8.0
+    k2 = (k.float() + u).to(torch.bfloat16)
+    assert torch.equal(k2.float(), k.float() + u)
+    scale = default_scale(d)
+    o1, l1 = _run(iofa.forward, q, k, v, scale, dev)
+    o2, l2 = _run(iofa.forward, q, k2, v, scale, dev)
+    shift = np.float32(scale) * (widen(q) @ u.double().numpy())
+    dl = l2.double().numpy() - l1.double().numpy()
+    assert np.abs(dl - shift).max() <= 2e-3 * max(1.0, np.abs(shift).max())
+    max_abs, rel_f, _ = errors(o2, None, widen(o1), None)
+    assert max_abs <= 1e-2 and rel_f <= 5e-3
+
+
+def test_deterministic(dev):
+    q, k, v, scale, _ = workload_qkv(2)
+    o1, l1 = _run(iofa.forward, q, k, v, scale, dev)
+    o2, l2 = _run(iofa.forward, q, k, v, scale, dev)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype,N,d", [("bf16", 8191, 128), ("fp16", 129, 64), ("fp32", 100, 128)])
+def test_no_writes_outside_outputs(dtype, N, d, dev):
+    B, H = 1, 2
+    q, k, v = (t.to(dev) for t in make_qkv(B, H, N, d, dtype, seed_base=5))
+    guard = 4096
+    n_o = B * H * N * d
+    obuf = torch.full((guard + n_o + guard,), float("nan"), dtype=DT[dtype], device=dev)
+    lbuf = torch.full((guard + B * H * N + guard,), -7.0, dtype=torch.float32, device=dev)
+    o = obuf[guard:guard + n_o].view(B, H, N, d)
+    lse = lbuf[guard:guard + B * H * N].view(B, H, N)
+    iofa.fa_fwd(q, k, v, o, lse, default_scale(d))
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[:guard]).all() and torch.isnan(obuf[-guard:]).all()
+    assert (lbuf[:guard] == -7.0).all() and (lbuf[-guard:] == -7.0).all()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_runs_on_caller_stream(dev):
+    q, k, v = (t.to(dev) for t in make_qkv(1, 2, 512, 128, "bf16", seed_base=3))
+    s = torch.cuda.Stream(device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 512, dtype=torch.float32, device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        iofa.fa_fwd(q, k, v, o, lse, default_scale(128), stream=s)
+    s.synchronize()
+    o_ref, lse_ref = oracle_full(q.cpu(), k.cpu(), v.cpu(), default_scale(128))
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, torch.bfloat16, "side stream")
+
+
+def test_errors_surface_through_binding(dev):
+    q, k, v = (t.to(dev) for t in make_qkv(1, 1, 64, 128, "bf16", seed_base=1))
+    lse = torch.empty(1, 1, 64, dtype=torch.float32, device=dev)
+    with pytest.raises(iofa.FaError) as ei:
+        iofa.fa_fwd(q, k, v, q, lse, 0.1)          # O aliases Q
+    assert ei.value.status == 7
+    with pytest.raises(iofa.FaError) as ei:
+        iofa.fa_fwd(q, k, v, torch.empty_like(q), lse, float("inf"))
+    assert ei.value.status == 6
+    q96 = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(iofa.FaError) as ei:
+        iofa.fa_fwd(q96, q96.clone(), q96.clone(), q96.clone(), lse, 0.1)
+    assert ei.value.status == 3
+
+
+# ----------------------------------------------------------- naive path
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+def test_naive_workload(idx, dev):
+    q, k, v, scale, spec = workload_qkv(idx)
+    _say(f"naive workload {idx}: {spec['name']}")
+    o, lse = _run(iofa.naive_forward, q, k, v, scale, dev)
+    N = spec["N"]
+    rows = np.arange(N) if idx in FULL_ORACLE else sample_rows(N, seed=idx)
+    if idx in FULL_ORACLE:
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+    else:
+        o_ref, lse_ref = oracle_rows(q, k, v, scale, rows)
+    res = errors(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref)
+    _say(f"  naive w{idx}: max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
+    assert_parity(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, q.dtype, f"naive w{idx}",
+                  tol=naive_tol(q.dtype, spec))
+
+
+def naive_tol(dtype, spec):
+    """The naive path stores S and P in the input type.  Rounding a score s
+    to that type moves it by up to u*|s| (u = 2^-8 bf16, 2^-11 fp16), which
+    changes its weight by the factor e^{u*|s|}; with |s| <= s_max that bounds
+    the error of O by about 2*u*s_max*max|V| on top of the fused bar.  The
+    normal workloads keep |s| below about 6; the stress workload reaches 60."""
+    base = dict(TOL[dtype])
+    if dtype == torch.float32:
+        return base
+    u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
+    s_max = 60.0 if spec.get("dist") == "stress" else 6.0
+    extra = 2.0 * u * s_max
+    return dict(o_abs=base["o_abs"] + extra, o_relf=base["o_relf"] + extra,
+                lse_abs=base["lse_abs"] + u * s_max)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_naive_ragged(dtype, dev):
+    for N in (1, 7, 64, 65, 200, 1000):
+        for d in (64, 128):
+            q, k, v = make_qkv(1, 2, N, d, dtype, seed_base=3 * N + d)
+            scale = default_scale(d)
+            _say(f"naive ragged {dtype} d={d} N={N}")
+            o, lse = _run(iofa.naive_forward, q, k, v, scale, dev)
+            o_ref, lse_ref = oracle_full(q, k, v, scale)
+            assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"naive {dtype} d={d} N={N}",
+                          tol=naive_tol(q.dtype, {}))
+
+
+def test_naive_without_lse(dev):
+    q, k, v = make_qkv(1, 2, 300, 64, "bf16", seed_base=8)
+    o, lse = _run(iofa.naive_forward, q, k, v, default_scale(64), dev, want_lse=False)
+    assert lse is None
+    o_ref, _ = oracle_full(q, k, v, default_scale(64))
+    max_abs, rel_f, _ = errors(o, None, o_ref, None)
+    assert max_abs <= 2e-2 and rel_f <= 1e-2
