@@ -96,7 +96,9 @@ def test_fused_other_scales(dev):
     for scale in (0.0, -0.125, 0.5):
         o, lse = _run(iofa.forward, q, k, v, scale, dev)
         o_ref, lse_ref = oracle_full(q, k, v, scale)
-        assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"scale={scale}")
+        # scale 0.5 at d=128 makes rows nearly one-hot, so |O| reaches ~3.5
+        assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"scale={scale}",
+                      output_rounding=True)
 
 
 # ------------------------------------------------------ invariants on GPU
@@ -190,23 +192,25 @@ def test_naive_workload(idx, dev):
     res = errors(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref)
     _say(f"  naive w{idx}: max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
     assert_parity(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, q.dtype, f"naive w{idx}",
-                  tol=naive_tol(q.dtype, spec))
+                  tol=naive_tol(q.dtype, lse_ref, v.float()))
 
 
-def naive_tol(dtype, spec):
+def naive_tol(dtype, lse_ref, v):
     """The naive path stores S and P in the input type.  Rounding a score s
-    to that type moves it by up to u*|s| (u = 2^-8 bf16, 2^-11 fp16), which
-    changes its weight by the factor e^{u*|s|}; with |s| <= s_max that bounds
-    the error of O by about 2*u*s_max*max|V| on top of the fused bar.  The
-    normal workloads keep |s| below about 6; the stress workload reaches 60."""
+    to that type moves it by up to u*|s| (u = 2^-8 bf16, 2^-11 fp16).  The
+    scores that carry weight lie below the row's LSE, so with
+    s_max = max|LSE| every weight changes by a factor within e^{+-2 u s_max}
+    and LSE by at most about 2 u s_max, and O (a weighted average of value
+    rows) by at most 2 u s_max max|V|.  Those terms are added to the fused
+    bar."""
     base = dict(TOL[dtype])
     if dtype == torch.float32:
         return base
     u = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -11
-    s_max = 60.0 if spec.get("dist") == "stress" else 6.0
-    extra = 2.0 * u * s_max
-    return dict(o_abs=base["o_abs"] + extra, o_relf=base["o_relf"] + extra,
-                lse_abs=base["lse_abs"] + u * s_max)
+    extra = 2.0 * u * float(np.abs(lse_ref).max())
+    vmax = float(v.abs().max())
+    return dict(o_abs=base["o_abs"] + vmax * extra, o_relf=base["o_relf"] + extra,
+                lse_abs=base["lse_abs"] + extra)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
@@ -219,7 +223,7 @@ def test_naive_ragged(dtype, dev):
             o, lse = _run(iofa.naive_forward, q, k, v, scale, dev)
             o_ref, lse_ref = oracle_full(q, k, v, scale)
             assert_parity(o, lse, o_ref, lse_ref, q.dtype, f"naive {dtype} d={d} N={N}",
-                          tol=naive_tol(q.dtype, {}))
+                          tol=naive_tol(q.dtype, lse_ref, v.float()))
 
 
 def test_naive_without_lse(dev):
