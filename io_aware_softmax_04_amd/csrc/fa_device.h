@@ -19,10 +19,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- types
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 struct Bf16 {
   using vec8 = bf16x8;
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+  // two floats -> two bf16 (round to nearest even) in one dword, lo first
+  __device__ static inline uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
   }
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -33,6 +41,9 @@ struct F16 {
   using vec8 = f16x8;
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+  __device__ static inline uint32_t pack(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
   }
   __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -137,7 +148,7 @@ struct VtTile {
   static constexpr int CH = D / 8;
   static constexpr int KPB = BC * CH / 256;
   static constexpr int NKG = BC / KPB;
-  static_assert(KPB == 2 || KPB == 4, "unsupported V tile shape");
+  static_assert(KPB == 1 || KPB == 2 || KPB == 4, "unsupported V tile shape");
   u32x4 r[KPB];
 
   __device__ inline void load(const uint16_t* __restrict__ base, int rows_valid,
@@ -164,10 +175,88 @@ struct VtTile {
         w[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
         w[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
         *reinterpret_cast<u32x2*>(dst) = w;
-      } else {
+      } else if constexpr (KPB == 2) {
         *reinterpret_cast<uint32_t*>(dst) = half_of(r[0], e) | (half_of(r[1], e) << 16);
+      } else {
+        *dst = static_cast<uint16_t>(half_of(r[0], e));
       }
     }
+  }
+};
+
+// ------------------------------------------- swizzled LDS tiles (fused path)
+//
+// K and V tiles of BC rows x D 16-bit elements are copied from global memory
+// straight into LDS with global_load_lds_dwordx4: one instruction moves 64
+// lanes x 16 bytes and writes them to 1 KiB of consecutive LDS bytes, lane l
+// at byte 16*l.  The tiles keep their row-major order; within a row the
+// 16-byte chunks are XOR-permuted so that the reads below hit 64 distinct
+// banks:
+//   K (read 16 B per lane, 16 rows per 16-lane group):
+//       chunk c of row r sits at c ^ (r & 15)         (D = 128)
+//                                c ^ ((r >> 1) & 7)   (D = 64)
+//   V (read with ds_read_b64_tr_b16, 4 rows x 32 B per 16-lane group):
+//       chunk c of row r sits at c ^ ((r & 3) << 2)          (D = 128)
+//                                c ^ (((r >> 1) & 1) << 2)   (D = 64)
+template <int D>
+__device__ inline int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ inline int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define IOFA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Per-lane part of the direct copies of one K or V tile.  Wave w writes the
+// 1 KiB blocks b = w + 4*i (i = 0 .. PER_WAVE-1); with this interleave the
+// swizzle of every row a lane copies is the same, so lane offsets differ
+// between blocks only by a constant.
+template <int D, int BC, bool IS_V>
+struct TileCopy {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROWS_PER_BLK = 64 / CH;     // rows in one 1 KiB block
+  static constexpr int BLKS = BC * D * 2 / 1024;   // 1 KiB blocks per tile
+  static constexpr int PER_WAVE = BLKS / 4;
+  static constexpr int ROW_STEP = 4 * ROWS_PER_BLK;  // rows between a lane's blocks
+  static_assert(PER_WAVE * 4 == BLKS, "tile must split over 4 waves");
+  int row0;   // row (inside the tile) this lane copies in block i = 0
+  int off0;   // element offset of that chunk inside the tile's rows
+  int lds0;   // element offset of block i = 0 inside the stage
+
+  __device__ inline void init(int wave, int lane) {
+    row0 = wave * ROWS_PER_BLK + lane / CH;
+    const int p = lane % CH;
+    const int c = p ^ (IS_V ? v_swz<D>(row0) : k_swz<D>(row0));
+    off0 = row0 * D + 8 * c;
+    lds0 = wave * 512;
+  }
+  // Copy rows k0 .. k0+BC-1 of `head` into `stage`.  With CLAMP, rows at or
+  // beyond N are read from row N-1 instead (always a valid address); their
+  // scores are masked to weight 0, so the duplicates never contribute.
+  template <bool CLAMP>
+  __device__ inline void issue(const uint16_t* __restrict__ head, int k0, int N,
+                               uint16_t* stage) const {
+    const uint16_t* base = head + static_cast<size_t>(k0) * D;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      int off = off0 + i * ROW_STEP * D;
+      if (CLAMP) {
+        const int over = k0 + row0 + i * ROW_STEP - (N - 1);
+        if (over > 0) off -= over * D;
+      }
+      __builtin_amdgcn_global_load_lds(base + off, IOFA_LDS(void, stage + lds0 + i * 2048), 16,
+                                       0, 0);
+    }
+  }
+  __device__ inline void copy(const uint16_t* __restrict__ head, int k0, int N,
+                              uint16_t* stage) const {
+    if (k0 + BC <= N)
+      issue<false>(head, k0, N, stage);
+    else
+      issue<true>(head, k0, N, stage);
   }
 };
 

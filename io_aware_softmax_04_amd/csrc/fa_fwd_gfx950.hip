@@ -27,30 +27,168 @@
 
 namespace iofa {
 
-template <int D>
+template <int D, int BC>
 struct FusedCfg {
   static constexpr int NW = 4;            // waves per workgroup
   static constexpr int BR = 32 * NW;      // query rows per workgroup
-  static constexpr int BC = 64;           // keys per tile
-  static constexpr int KS = D + 8;        // K row stride in LDS (elements)
-  static constexpr int VS = BC + 8;       // transposed-V row stride (elements)
-  static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int SB = BC / 32;      // 32-key score blocks per K/V tile
+  static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
+  static constexpr int TILE = BC * D;     // elements of one K or V tile
+  static constexpr int SMEM = 4 * TILE;   // two K stages, two V stages
 };
 
-template <class T, int D>
+// The running maximum is only moved when a tile's maximum exceeds it by more
+// than this many log2 units.  The result o = z / l and the log-sum-exp
+// m + log2 l hold for any reference value m; keeping m within 8 of the true
+// maximum bounds every exponential by 2^8, and the O accumulator is then
+// rescaled only on the (rare, wave-uniform) tiles that move m.
+constexpr float kRescaleSlack = 8.0f;
+
+// One wave's share of the online-softmax recurrence.
+template <class T, int D, int BC>
+struct WaveState {
+  using C = FusedCfg<D, BC>;
+  typename T::vec8 qf[D / 16];   // Q fragments (B operand of S^T = K Q^T)
+  f32x16 o[D / 32];              // O^T accumulator: lane owns one query column
+  float m_run;                   // reference maximum, log2 units of scaled scores
+  float l_run;                   // denominator relative to m_run
+  int k_row;                     // this lane's K row inside a 32-row block
+  int k_swz;                     // its chunk swizzle
+  int hi;                        // lane half (0: lanes 0-31, 1: lanes 32-63)
+  int v_off[D / 32];             // byte-free element offsets of this lane's
+                                 // transposed-read address per 32-column block
+
+  __device__ inline void init_lanes(int lane) {
+    const int l32 = lane & 31;
+    hi = lane >> 5;
+    k_row = l32;
+    k_swz = k_swz_of(l32);
+    // ds_read_b64_tr_b16: in each 16-lane group, lane t supplies row
+    // key0 + t/4, columns c0 + 4*(t%4) .. +3 and receives column c0 + t of
+    // rows key0 .. key0+3.  Group g = lane/16 covers lane half g/2 (keys
+    // 4*(g/2) + ...) and column half g%2.
+    const int g = lane >> 4, t = lane & 15;
+    const int row = 4 * (g >> 1) + (t >> 2);
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
+      const int chunk = (col >> 3) ^ v_swz<D>(row);
+      v_off[cb] = row * D + chunk * 8 + (col & 7);
+    }
+  }
+  __device__ static inline int k_swz_of(int r) { return iofa::k_swz<D>(r); }
+
+  // a3: S^T block scores of one tile from a K stage (raw dot products)
+  __device__ inline void scores(f32x16 (&s)[C::SB], const uint16_t* Ks) const {
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) s[sb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int chunk = (2 * kk + hi) ^ k_swz;
+#pragma unroll
+      for (int sb = 0; sb < C::SB; ++sb) {
+        const auto a = lds_vec8<T>(Ks + (32 * sb + k_row) * D + chunk * 8);
+        s[sb] = T::mfma(a, qf[kk], s[sb]);
+      }
+    }
+  }
+
+  // a4 + a5: tile maximum, reference-maximum update, exponentials, row sum;
+  // returns P rounded to the input type as the B operand of KSTEPS products.
+  // Branch-free, so the scheduler can interleave it with independent MFMAs.
+  // TAIL masks keys at or beyond keys_valid to weight 0.
+  template <bool TAIL>
+  __device__ inline float softmax(f32x16 (&s)[C::SB], typename T::vec8 (&pk)[C::KSTEPS],
+                                  float c2, int keys_valid) {
+    float mraw = -__builtin_inff();
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (TAIL) {
+          const int key = 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          mraw = (key < keys_valid) ? fmaxf(mraw, s[sb][r]) : mraw;
+        } else {
+          mraw = fmaxf(mraw, s[sb][r]);
+        }
+      }
+    mraw = halfwave_max(mraw);
+    const float mt = mraw * c2;          // this tile's maximum, log2 units (c2 >= 0)
+    const bool move = mt > m_run + kRescaleSlack;   // always on the first tile
+    const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+    m_run = move ? mt : m_run;
+    const float msub = m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[sb][r], c2, -msub));
+        if (TAIL) {
+          const int key = 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          p = (key < keys_valid) ? p : 0.f;
+        }
+        s[sb][r] = p;
+        rs += p;
+      }
+    }
+    rs = halfwave_sum(rs);
+    l_run = alpha * l_run + rs;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const f32x16& p = s[ks >> 1];
+      const int b = 8 * (ks & 1);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = T::pack(p[b + 2 * e], p[b + 2 * e + 1]);
+      pk[ks] = __builtin_bit_cast(typename T::vec8, w);
+    }
+    return alpha;
+  }
+
+  // a6: acc = alpha * acc + P V_j.  The A operand (V^T) comes from two
+  // transposed reads: keys 16*ks + 4*hi + 0..3 and 16*ks + 8 + 4*hi + 0..3,
+  // the same keys the P registers hold in k-slots 0..3 and 4..7.
+  __device__ inline void accumulate(const typename T::vec8 (&pk)[C::KSTEPS], float alpha,
+                                    const uint16_t* Vs) {
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const uint16_t* p0 = Vs + v_off[cb] + (16 * ks) * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(IOFA_LDS(s16x4, p0));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(IOFA_LDS(s16x4, p0 + 8 * D));
+        const auto a = __builtin_bit_cast(typename T::vec8,
+                                          __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[cb] = T::mfma(a, pk[ks], o[cb]);
+      }
+    }
+  }
+};
+
+// Workgroup schedule with two K stages and two V stages in LDS.  While tile j
+// is processed (its scores were computed during tile j-1), the wave computes
+// the scores of tile j+1 from K stage (j+1)%2 -- independent work the
+// scheduler interleaves with tile j's softmax -- and multiplies P_j with V
+// stage j%2.  Direct global-to-LDS copies of K_{j+2} and V_{j+1} are issued
+// at the top of tile j into the two stages no wave reads during tile j
+// (K stage j%2, V stage (j+1)%2) and awaited before the one barrier per tile.
+template <class T, int D, int BC>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int N, int num_qtiles, int num_wg, float scale) {
-  using C = FusedCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+  using C = FusedCfg<D, BC>;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[C::SMEM];
+  uint16_t* const kst[2] = {smem, smem + C::TILE};
+  uint16_t* const vst[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
 
   const int L = xcd_logical_id(blockIdx.x, num_wg);
   const int bh = L / num_qtiles, qt = L % num_qtiles;
@@ -59,139 +197,92 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  // a1: this lane's query row and its Q fragments (B operand of S^T = K Q^T)
-  const int q = qt * C::BR + wave * 32 + l32;
-  typename T::vec8 qf[D / 16];
+  // a2 prologue: K_0, V_0, K_1 copies in flight while Q is loaded
+  const int ntiles = (N + BC - 1) / BC;
+  TileCopy<D, BC, false> kcp;
+  TileCopy<D, BC, true> vcp;
+  kcp.init(wave, lane);
+  vcp.init(wave, lane);
+  kcp.copy(Kh, 0, N, kst[0]);
+  vcp.copy(Vh, 0, N, vst[0]);
+  if (ntiles > 1) kcp.copy(Kh, BC, N, kst[1]);
+
+  // a1: this lane's query row, its Q fragments, the running state.  A
+  // negative scale is folded into Q (negation is exact) so the scale applied
+  // to the fp32 scores is c2 = |scale| * log2(e) >= 0.
+  WaveState<T, D, BC> ws;
+  ws.init_lanes(lane);
+  const int q = qt * C::BR + wave * 32 + (lane & 31);
+  const uint32_t flip = scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    if (q < N)
-      qf[kk] = gmem_vec8<T>(Qh + static_cast<size_t>(q) * D + 16 * kk + 8 * hi);
-    else
-      qf[kk] = __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (q < N) w = *reinterpret_cast<const u32x4*>(Qh + static_cast<size_t>(q) * D + 16 * kk + 8 * ws.hi);
+    w ^= flip;
+    ws.qf[kk] = __builtin_bit_cast(typename T::vec8, w);
   }
-
-  f32x16 o[D / 32];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
-  float m_run = -__builtin_inff();   // running max, log2 units of scaled scores
-  float l_run = 0.f;                 // running denominator
-  const float c2 = scale * kLog2e;
+  for (int cb = 0; cb < D / 32; ++cb) ws.o[cb] = f32x16{};
+  ws.m_run = -__builtin_inff();
+  ws.l_run = 0.f;
+  const float c2 = fabsf(scale) * kLog2e;
 
-  RowTile<D, C::BC, C::KS> kt;
-  VtTile<D, C::BC, C::VS, true> vt;
-  const int ntiles = (N + C::BC - 1) / C::BC;
-
-  // a2: first K/V tile into stage 0
-  kt.load(Kh, N, tid);
-  vt.load(Vh, N, tid);
-  kt.store(smem, tid);
-  vt.store(smem + C::K_ELEMS, tid);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sa[C::SB], sb[C::SB];
+  ws.scores(sa, kst[0]);
+  __syncthreads();   // K stage 0 is refilled during tile 0
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * C::BC;
-    const bool more = j + 1 < ntiles;
-    if (more) {  // a2: next tile's global loads in flight during this tile
-      kt.load(Kh + static_cast<size_t>(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-      vt.load(Vh + static_cast<size_t>(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-    }
-    const uint16_t* Ks = smem + (j & 1) * C::STAGE;
-    const uint16_t* Vt = Ks + C::K_ELEMS;
-
-    // a3: S^T for 64 keys x 32 queries, two 32-key blocks
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // One tile: softmax of tile j interleaved with the scores of tile j+1
+  // (from K stage (j+1)%2; on the last tile these read a stale stage and are
+  // discarded), then P_j V_j.
+  auto tile = [&](int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB]) {
+    const int k0 = j * BC;
+    if (j + 2 < ntiles) kcp.copy(Kh, k0 + 2 * BC, N, kst[j & 1]);
+    if (j + 1 < ntiles) vcp.copy(Vh, k0 + BC, N, vst[(j + 1) & 1]);
+    typename T::vec8 pk[C::KSTEPS];
+    float alpha;
+    if (k0 + BC <= N) {
+      alpha = ws.template softmax<false>(s_cur, pk, c2, BC);
+      ws.scores(s_nxt, kst[(j + 1) & 1]);
+      // interleave: per score MFMA, its K fragment read and a slice of the
+      // softmax's vector work
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const auto a = lds_vec8<T>(Ks + (32 * sb + l32) * C::KS + 16 * kk + 8 * hi);
-        s[sb] = T::mfma(a, qf[kk], s[sb]);
+      for (int i = 0; i < D / 16 * C::SB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
       }
+    } else {
+      alpha = ws.template softmax<true>(s_cur, pk, c2, N - k0);
+      ws.scores(s_nxt, kst[(j + 1) & 1]);
     }
-
-    // scale into log2 units; keys beyond N get -inf (weight 0)
-    float x[32];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[16 * sb + r] = s[sb][r] * c2;
-    if (k0 + C::BC > N) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N) x[16 * sb + r] = -__builtin_inff();
-        }
-    }
-
-    // a4: row max over this tile, merged with the running max
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = halfwave_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float msub = (m_new == -__builtin_inff()) ? 0.f : m_new;
-
-    // a5: exponentials, rescale factor, denominator
-    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = __builtin_amdgcn_exp2f(x[i] - msub);
-      rs += x[i];
-    }
-    rs = halfwave_sum(rs);
-    l_run = alpha * l_run + rs;
-    m_run = m_new;
-
-    // P rounded to the input type, as the B operand of four 16-key steps
-    typename T::vec8 pk[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = pack2(T::bits(x[8 * ks + 2 * e]), T::bits(x[8 * ks + 2 * e + 1]));
-      pk[ks] = __builtin_bit_cast(typename T::vec8, w);
-    }
-
-    // a6: acc = alpha * acc + P V
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const auto a = lds_vec8<T>(Vt + (32 * cb + l32) * C::VS + 16 * ks + 8 * hi);
-        o[cb] = T::mfma(a, pk[ks], o[cb]);
-      }
-    }
-
-    if (more) {
-      uint16_t* nxt = smem + ((j + 1) & 1) * C::STAGE;
-      kt.store(nxt, tid);
-      vt.store(nxt + C::K_ELEMS, tid);
-    }
+    ws.accumulate(pk, alpha, vst[j & 1]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, sa, sb);
+    if (j + 1 < ntiles) tile(j + 1, sb, sa);
   }
 
-  // a7: O = acc / l rounded to the input type; LSE = m + ln l (natural log)
+  // a7: O = acc / l rounded to the input type; LSE = ln2 * (m + log2 l)
   if (q < N) {
-    const float inv_l = 1.0f / l_run;
+    const float inv_l = 1.0f / ws.l_run;
     uint16_t* Oq = O + head + static_cast<size_t>(q) * D;
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack2(T::bits(o[cb][4 * g + 0] * inv_l), T::bits(o[cb][4 * g + 1] * inv_l));
-        w[1] = pack2(T::bits(o[cb][4 * g + 2] * inv_l), T::bits(o[cb][4 * g + 3] * inv_l));
-        *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * hi) = w;
+        w[0] = T::pack(ws.o[cb][4 * g + 0] * inv_l, ws.o[cb][4 * g + 1] * inv_l);
+        w[1] = T::pack(ws.o[cb][4 * g + 2] * inv_l, ws.o[cb][4 * g + 3] * inv_l);
+        *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * ws.hi) = w;
       }
     }
-    if (hi == 0)
-      LSE[static_cast<size_t>(bh) * N + q] = (m_run + __builtin_amdgcn_logf(l_run)) * kLn2;
+    if (ws.hi == 0)
+      LSE[static_cast<size_t>(bh) * N + q] =
+          (ws.m_run + __builtin_amdgcn_logf(ws.l_run)) * kLn2;
   }
 }
 
@@ -284,12 +375,12 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
 
 // ------------------------------------------------------------- launchers
 
-template <class T, int D>
+template <class T, int D, int BC = 64>
 static hipError_t launch16(const FwdArgs& a) {
-  using C = FusedCfg<D>;
+  using C = FusedCfg<D, BC>;
   const int qtiles = static_cast<int>((a.N + C::BR - 1) / C::BR);
   const int64_t wg = a.BH * qtiles;
-  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
                      a.stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
                      static_cast<const uint16_t*>(a.V), static_cast<uint16_t*>(a.O), a.LSE,
                      static_cast<int>(a.N), qtiles, static_cast<int>(wg), a.scale);
@@ -308,7 +399,7 @@ static hipError_t launch32(const FwdArgs& a) {
 }
 
 int64_t fused_workgroups(int dtype, int64_t BH, int64_t N) {
-  const int64_t br = (dtype == kDtypeF32) ? 32 : FusedCfg<128>::BR;
+  const int64_t br = (dtype == kDtypeF32) ? 32 : FusedCfg<128, 64>::BR;
   return BH * ((N + br - 1) / br);
 }
 
