@@ -28,7 +28,10 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 FLOP/
 PEAK_HBM_GBS = 8000.0
 FUSED_KERNEL_SOURCES = ["io_aware_softmax_04_amd/csrc/fa_fwd_gfx950.hip",
                         "io_aware_softmax_04_amd/csrc/fa_device.h"]
-TRAFFIC_FILE = "profiles/traffic_fused_fwd_{tag}.json"
+TRAFFIC_FILE = "profiles/traffic_fused_fwd_{tag}.md"
+FUSED_KERNEL_NAME = "fa_fwd_16_kernel"
+COPY_KERNEL_NAME = "__amd_rocclr_copyBuffer"
+NAIVE_KERNEL_NAMES = ["naive_scores_16", "naive_softmax_16", "naive_pv_16"]
 
 
 def parse():
@@ -43,6 +46,17 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run a device copy of this many MiB (counter calibration)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "`bench.py --calibrate-copy-mib M` into the traffic summary under "
+                        "profiles/ and exit (no GPU needed)")
+    p.add_argument("--trace-from", metavar="TRACE_DIR",
+                   help="summarise a `rocprofv3 --kernel-trace --stats` run of bench.py "
+                        "into the kernel-trace summary under profiles/ and exit")
+    p.add_argument("--trace-cmd", default="",
+                   help="the bench.py arguments of that run (recorded in the summary)")
+    p.add_argument("--copy-mib", type=int, default=1024,
+                   help="size of the calibration copy in those runs")
     return p.parse_args()
 
 
@@ -68,6 +82,178 @@ def bytes_models(spec, br=128):
         "tiled_io_model": heads * (e * (2 * N * d + 2 * N * d * math.ceil(N / br)) + 4 * N),
         "naive_model": heads * e * (4 * N * d + 4 * N * N),
     }
+
+
+def _counter_rows(directory, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f, encoding="utf-8") as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
+    """HBM-side bytes of the fused kernel from the FETCH_SIZE and WRITE_SIZE
+    counters (KiB per dispatch), each scaled so that a device copy of
+    ``copy_mib`` MiB reads and writes exactly that many bytes."""
+    copy_bytes = copy_mib * (1 << 20)
+    out = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(directory, counter)
+        fused = [float(r["Counter_Value"]) for r in rows if FUSED_KERNEL_NAME in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_NAME in r["Kernel_Name"]]
+        if not fused or not copy:
+            raise SystemExit(f"{counter}: fused or calibration-copy dispatches missing")
+        factor = copy_bytes / (sum(copy) / len(copy) * 1024)
+        kib = sum(fused) / len(fused)
+        out[counter] = dict(kib=kib, factor=factor, bytes=kib * 1024 * factor,
+                            dispatches=len(fused), copy_kib=sum(copy) / len(copy))
+    total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    # the naive contrast's three kernels, if the runs included them
+    naive = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _counter_rows(directory, counter):
+            for kname in NAIVE_KERNEL_NAMES:
+                if kname in r["Kernel_Name"]:
+                    naive.setdefault(kname, {}).setdefault(counter, []).append(
+                        float(r["Counter_Value"]) * 1024 * out[counter]["factor"])
+    models = bytes_models(spec)
+    tag = workload_tag(spec)
+    lines = [
+        f"# HBM traffic of the fused forward, {spec['name']}",
+        "",
+        "Commands (one MI355X, from the repository root; one counter per run):",
+        "",
+        "```",
+        f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
+        f"python bench.py --workload {index} --steps 3 --warmup 1 "
+        f"--no-cpu-baseline --calibrate-copy-mib {copy_mib}",
+        f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv -- "
+        f"python bench.py --workload {index} --steps 3 --warmup 1 "
+        f"--no-cpu-baseline --calibrate-copy-mib {copy_mib}",
+        f"python bench.py --workload {index} --traffic-from "
+        f"{fetch_dir} {write_dir} --copy-mib {copy_mib}",
+        "```",
+        "",
+        f"Calibration: a device copy of {copy_mib} MiB ({COPY_KERNEL_NAME}) reads "
+        f"{out['FETCH_SIZE']['copy_kib']:.1f} KiB on FETCH_SIZE and writes "
+        f"{out['WRITE_SIZE']['copy_kib']:.1f} KiB on WRITE_SIZE, so the counters are "
+        f"scaled by {out['FETCH_SIZE']['factor']:.4f} (fetch) and "
+        f"{out['WRITE_SIZE']['factor']:.4f} (write).",
+        "",
+        "| counter | KiB / dispatch (raw) | dispatches | scale | bytes / launch |",
+        "|---|---|---|---|---|",
+    ]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        r = out[c]
+        lines.append(f"| {c} | {r['kib']:.2f} | {r['dispatches']} | {r['factor']:.4f} | "
+                     f"{r['bytes']:.0f} |")
+    lines += [
+        "",
+        f"Total {total:.0f} bytes per launch: {total / models['compulsory']:.3f} x the "
+        f"compulsory bytes ({models['compulsory']}), {total / models['tiled_io_model']:.4f} x "
+        f"the tiled-IO model at Br=128 ({models['tiled_io_model']}), "
+        f"{total / models['naive_model']:.4f} x the naive model ({models['naive_model']}).",
+        "",
+    ]
+    if naive:
+        lines += [
+            "Naive three-kernel contrast in the same runs (bytes per launch, scaled as above):",
+            "",
+            "| kernel | read | written | total |",
+            "|---|---|---|---|",
+        ]
+        ntotal = 0.0
+        for kname in NAIVE_KERNEL_NAMES:
+            if kname not in naive:
+                continue
+            rd = sum(naive[kname]["FETCH_SIZE"]) / len(naive[kname]["FETCH_SIZE"])
+            wr = sum(naive[kname]["WRITE_SIZE"]) / len(naive[kname]["WRITE_SIZE"])
+            ntotal += rd + wr
+            lines.append(f"| {kname} | {rd:.0f} | {wr:.0f} | {rd + wr:.0f} |")
+        lines += [
+            "",
+            f"Naive total {ntotal:.0f} bytes = {ntotal / models['naive_model']:.3f} x the "
+            f"element-count model e*B*H*(4Nd + 4N^2) = {models['naive_model']}; the fused "
+            f"kernel moves {total / ntotal:.4f} x the naive path's bytes.",
+            "",
+        ]
+    lines += [
+        "Machine-readable (bench.py reads these two lines; the hash covers the fused "
+        "kernel's sources, so the figure is dropped once the kernel changes):",
+        "",
+        f"bytes_per_launch: {total:.0f}",
+        f"kernel_sources_sha256_16: {sources_hash()}",
+        "",
+    ]
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(tag=tag))
+    with open(path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    print(path)
+
+
+def summarise_trace(trace_dir, index, spec, bench_args):
+    """Per-kernel durations from rocprofv3's kernel_stats.csv, with the
+    fused kernel's rate at the algorithmic FLOP count."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    with open(files[0], encoding="utf-8") as fh:
+        rows = list(csv.DictReader(fh))
+    flops = 4.0 * spec["B"] * spec["H"] * spec["N"] ** 2 * spec["d"]
+    tag = workload_tag(spec)
+    lines = [
+        f"# Kernel trace, {spec['name']}",
+        "",
+        "Command (one MI355X, from the repository root):",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run --output-format csv -- "
+        f"python bench.py {bench_args}",
+        f"python bench.py --workload {index} --trace-from {trace_dir} --trace-cmd '{bench_args}'",
+        "```",
+        "",
+        "| kernel | calls | average (ns) | min (ns) | max (ns) | TFLOP/s at 4BHN^2d |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        name = r["Name"]
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        short = short.replace("void ", "").replace("iofa::", "")
+        rate = ""
+        if FUSED_KERNEL_NAME in name:
+            rate = f"{flops / (float(r['AverageNs']) * 1e-9) / 1e12:.1f}"
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | {rate} |")
+    lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
+    path = os.path.join(ROOT, f"profiles/kernel_trace_{tag}.md")
+    with open(path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    print(path)
+
+
+def read_traffic(spec):
+    """bytes_per_launch from the committed traffic summary, or None when it is
+    missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(tag=workload_tag(spec)))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path, encoding="utf-8") as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith(("|", "#", "`")):
+                key, _, val = ln.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_sha256_16") != sources_hash():
+        return None
+    return int(fields["bytes_per_launch"])
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -139,6 +325,15 @@ def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
 
 def main():
     args = parse()
+    if args.trace_from:
+        from workloads import WORKLOADS
+        summarise_trace(args.trace_from, args.workload, WORKLOADS[args.workload], args.trace_cmd)
+        return
+    if args.traffic_from:
+        from workloads import WORKLOADS
+        summarise_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_mib,
+                          args.workload, WORKLOADS[args.workload])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by "
               "heads with no communication and is measured on one GPU's share.",
@@ -178,13 +373,7 @@ def main():
     value = flops / (wall_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if spec["dtype"] in ("bf16", "fp16") else 157.3
 
-    traffic = None
-    tpath = os.path.join(ROOT, TRAFFIC_FILE.format(tag=workload_tag(spec)))
-    if os.path.exists(tpath):
-        with open(tpath, encoding="utf-8") as fh:
-            rec = json.load(fh)
-        if rec.get("kernel_sources_sha256_16") == sources_hash():
-            traffic = rec.get("bytes_per_launch")
+    traffic = read_traffic(spec)
 
     models = bytes_models(spec)
     line = {
