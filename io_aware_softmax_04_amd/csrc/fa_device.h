@@ -187,9 +187,9 @@ struct VtTile {
 // ------------------------------------------- swizzled LDS tiles (fused path)
 //
 // K and V tiles of BC rows x D 16-bit elements are copied from global memory
-// straight into LDS with global_load_lds_dwordx4: one instruction moves 64
-// lanes x 16 bytes and writes them to 1 KiB of consecutive LDS bytes, lane l
-// at byte 16*l.  The tiles keep their row-major order; within a row the
+// straight into LDS with buffer_load_dwordx4 ... lds: one instruction moves
+// 64 lanes x 16 bytes and writes them to 1 KiB of consecutive LDS bytes, lane
+// l at byte 16*l.  The tiles keep their row-major order; within a row the
 // 16-byte chunks are XOR-permuted so that the reads below hit 64 distinct
 // banks:
 //   K (read 16 B per lane, 16 rows per 16-lane group):
@@ -210,10 +210,48 @@ __device__ inline int v_swz(int row) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define IOFA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// Per-lane part of the direct copies of one K or V tile.  Wave w writes the
-// 1 KiB blocks b = w + 4*i (i = 0 .. PER_WAVE-1); with this interleave the
-// swizzle of every row a lane copies is the same, so lane offsets differ
-// between blocks only by a constant.
+// One buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes, lane l from byte
+// voff of the buffer `rsrc`, into 1 KiB of consecutive LDS bytes at
+// lds_byte (lane l at lds_byte + 16*l).  Loads at or beyond the buffer's
+// byte length return zeros.  Issued as inline assembly so the compiler does
+// not track it: it would otherwise wait for every such copy before any LDS
+// read (it cannot tell which LDS bytes a copy writes).  The caller orders it
+// with explicit waits on the vector-memory counter before the copied bytes
+// are read or the workgroup ends.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_byte)
+               : "memory");
+}
+
+// Raw buffer over `bytes` bytes at p (range-checked loads; word 3 selects
+// the 32-bit data format gfx9 buffers need for raw accesses).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+__device__ inline uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(IOFA_LDS(const void, p)));
+}
+
+// s_waitcnt with only the vector-memory counter constrained: wait until at
+// most n vector memory operations of this wave are outstanding.
+template <int n>
+__device__ inline void wait_vmem() {
+  static_assert(n >= 0 && n < 64, "vmcnt out of range");
+  // gfx9 encoding: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
+  // (15 = no wait), vmcnt[5:4] in bits 15:14
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Per-lane part of the direct copies of one K or V tile (BC rows x D 16-bit
+// elements, row-major, chunks swizzled as above) from global memory into an
+// LDS stage.  Wave w writes the 1 KiB blocks b = w + 4*i (i = 0 ..
+// PER_WAVE-1); with this interleave the swizzle of every row a lane copies
+// is the same, and lane offsets differ between blocks only by a constant.
 template <int D, int BC, bool IS_V>
 struct TileCopy {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
@@ -222,43 +260,38 @@ struct TileCopy {
   static constexpr int PER_WAVE = BLKS / 4;
   static constexpr int ROW_STEP = 4 * ROWS_PER_BLK;  // rows between a lane's blocks
   static_assert(PER_WAVE * 4 == BLKS, "tile must split over 4 waves");
-  int row0;   // row (inside the tile) this lane copies in block i = 0
-  int off0;   // element offset of that chunk inside the tile's rows
-  int lds0;   // element offset of block i = 0 inside the stage
+  uint32_t voff0;     // byte offset of this lane's chunk in block i = 0
+  uint32_t lds_wave;  // byte offset of block i = 0 inside a stage (wave-uniform)
 
+  // `wave` must be wave-uniform (read with readfirstlane by the caller).
   __device__ inline void init(int wave, int lane) {
-    row0 = wave * ROWS_PER_BLK + lane / CH;
+    const int row0 = wave * ROWS_PER_BLK + lane / CH;
     const int p = lane % CH;
     const int c = p ^ (IS_V ? v_swz<D>(row0) : k_swz<D>(row0));
-    off0 = row0 * D + 8 * c;
-    lds0 = wave * 512;
+    voff0 = static_cast<uint32_t>(row0 * D + 8 * c) * 2u;
+    lds_wave = static_cast<uint32_t>(wave) * 1024u;
   }
-  // Copy rows k0 .. k0+BC-1 of `head` into `stage`.  With CLAMP, rows at or
-  // beyond N are read from row N-1 instead (always a valid address); their
-  // scores are masked to weight 0, so the duplicates never contribute.
-  template <bool CLAMP>
-  __device__ inline void issue(const uint16_t* __restrict__ head, int k0, int N,
-                               uint16_t* stage) const {
-    const uint16_t* base = head + static_cast<size_t>(k0) * D;
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      int off = off0 + i * ROW_STEP * D;
-      if (CLAMP) {
-        const int over = k0 + row0 + i * ROW_STEP - (N - 1);
-        if (over > 0) off -= over * D;
-      }
-      __builtin_amdgcn_global_load_lds(base + off, IOFA_LDS(void, stage + lds0 + i * 2048), 16,
-                                       0, 0);
-    }
-  }
+  // Rows k0 .. k0+BC-1 of `head` (N rows) into the stage at LDS byte
+  // address stage_byte.  Rows at or beyond N (also whole tiles past the
+  // end) arrive as zeros.
   __device__ inline void copy(const uint16_t* __restrict__ head, int k0, int N,
-                              uint16_t* stage) const {
-    if (k0 + BC <= N)
-      issue<false>(head, k0, N, stage);
-    else
-      issue<true>(head, k0, N, stage);
+                              uint32_t stage_byte) const {
+    const int rows = N - k0 > 0 ? N - k0 : 0;
+    const auto rsrc = buffer_rsrc(head + static_cast<size_t>(k0) * D,
+                                  static_cast<uint32_t>(rows) * (D * 2u));
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      lds_dma16(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * 4096u);
   }
 };
+
+// 16-byte and transposing 8-byte LDS reads at a byte address.
+__device__ inline u32x4 lds_read16(uint32_t byte) {
+  return *IOFA_LDS(const u32x4, static_cast<uintptr_t>(byte));
+}
+__device__ inline s16x4 lds_read_tr8(uint32_t byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(IOFA_LDS(s16x4, static_cast<uintptr_t>(byte)));
+}
 
 template <class T>
 __device__ inline typename T::vec8 lds_vec8(const uint16_t* p) {

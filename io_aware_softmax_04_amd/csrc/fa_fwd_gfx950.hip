@@ -8,20 +8,28 @@
 // "核心思想" (blocks of the matrices staged in fast on-chip memory).
 //
 // gfx950 mapping (16-bit inputs):
-//   * workgroup = 4 waves = 128 query rows of one head; each wave owns 32
-//     query rows for the whole key sweep;
-//   * the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (fp32 acc): the
-//     accumulator then gives each lane one query column, so the row max and
-//     row sum are in-lane over 32 scores plus one exchange with the lane 32
-//     apart (v_permlane32_swap);
-//   * O^T = V^T P^T uses the same registers as the B operand (P rounded to
-//     the input type), so P never leaves the lane; the rescale by
-//     e^{m_old - m_new} and the final 1/l are in-lane too;
-//   * K tiles (64 keys) sit row-major in LDS; V tiles sit transposed (one LDS
-//     row per output column) so each lane reads its 8 keys as 16 bytes;
-//   * K/V tiles are double-buffered: the next tile's global loads are in
-//     flight while the current tile is multiplied; one barrier per tile;
-//   * exponentials are exp2 with log2(e) folded into the fp32 scale.
+//   * workgroup = 4 waves = 128 query rows of one head, two workgroups per
+//     CU (8 waves, two per SIMD); each wave owns 32 query rows for the whole
+//     key sweep and keeps their Q fragments in VGPRs;
+//   * the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (fp32 acc): each
+//     lane then holds one query column, so the row max and row sum are
+//     in-lane over the tile's scores plus one exchange with the lane 32 apart
+//     (v_permlane32_swap);
+//   * O^T = V^T P^T takes P (rounded to the input type) straight from the
+//     same registers as its B operand; V^T fragments come from the row-major
+//     V tile through the transposing ds_read_b64_tr_b16;
+//   * K and V tiles (32 keys at d = 128, 64 at d = 64) are copied global ->
+//     LDS directly (buffer_load_dwordx4 ... lds, swizzled rows, range-checked
+//     so rows past N arrive as zeros) into two stages each;
+//   * three-stage software pipeline: while the VALU computes the softmax of
+//     tile j, the MFMA unit runs P_{j-1} V_{j-1} and the scores of tile j+1,
+//     none of which depend on that softmax; one barrier per tile;
+//   * the loop is unrolled by two so every LDS stage offset is a constant:
+//     each LDS read is a per-lane address computed once plus an immediate;
+//   * exponentials are exp2 with log2(e) folded into the fp32 scale; the row
+//     sum adds the fp32 exponentials, so the log-sum-exp keeps fp32 accuracy.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -31,10 +39,11 @@ template <int D, int BC>
 struct FusedCfg {
   static constexpr int NW = 4;            // waves per workgroup
   static constexpr int BR = 32 * NW;      // query rows per workgroup
-  static constexpr int SB = BC / 32;      // 32-key score blocks per K/V tile
+  static constexpr int SB = BC / 32;      // 32-key score blocks per tile
   static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
-  static constexpr int TILE = BC * D;     // elements of one K or V tile
-  static constexpr int SMEM = 4 * TILE;   // two K stages, two V stages
+  static constexpr int TILE = BC * D;     // elements of one K or V stage
+  static constexpr uint32_t TB = TILE * 2u;   // bytes of one stage
+  static constexpr int SMEM = 4 * TILE;   // K stages 0, 1, then V stages 0, 1
 };
 
 // The running maximum is only moved when a tile's maximum exceeds it by more
@@ -48,58 +57,81 @@ constexpr float kRescaleSlack = 8.0f;
 template <class T, int D, int BC>
 struct WaveState {
   using C = FusedCfg<D, BC>;
-  typename T::vec8 qf[D / 16];   // Q fragments (B operand of S^T = K Q^T)
+  using vec8 = typename T::vec8;
+  vec8 qf[D / 16];               // Q fragments (B operand of S^T = K Q^T)
   f32x16 o[D / 32];              // O^T accumulator: lane owns one query column
   float m_run;                   // reference maximum, log2 units of scaled scores
   float l_run;                   // denominator relative to m_run
-  int k_row;                     // this lane's K row inside a 32-row block
-  int k_swz;                     // its chunk swizzle
   int hi;                        // lane half (0: lanes 0-31, 1: lanes 32-63)
-  int v_off[D / 32];             // byte-free element offsets of this lane's
-                                 // transposed-read address per 32-column block
+  uint32_t k_addr[D / 16];       // LDS byte address of the K fragment, stage 0
+  uint32_t v_addr[D / 32];       // LDS byte address of the V^T read, stage 0
 
-  __device__ inline void init_lanes(int lane) {
+  // smem_byte: LDS byte address of the stage area (K stage 0).
+  __device__ inline void init_lanes(int lane, uint32_t smem_byte) {
     const int l32 = lane & 31;
     hi = lane >> 5;
-    k_row = l32;
-    k_swz = k_swz_of(l32);
-    // ds_read_b64_tr_b16: in each 16-lane group, lane t supplies row
+    // K: lane (l32, hi) reads key row l32 (+32 per score block), columns
+    // 16*kk + 8*hi .. +7, i.e. chunk 2*kk + hi, stored at chunk
+    // (2*kk + hi) ^ k_swz(row); the swizzle is the same for row + 32.
+    const int kswz = k_swz<D>(l32);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      k_addr[kk] = smem_byte + static_cast<uint32_t>(l32 * D + (((2 * kk + hi) ^ kswz) * 8)) * 2u;
+    // V: ds_read_b64_tr_b16: in each 16-lane group, lane t supplies row
     // key0 + t/4, columns c0 + 4*(t%4) .. +3 and receives column c0 + t of
     // rows key0 .. key0+3.  Group g = lane/16 covers lane half g/2 (keys
-    // 4*(g/2) + ...) and column half g%2.
+    // 4*(g/2) + ...) and column half g%2.  The swizzle depends on row % 4,
+    // the same for every key step.
     const int g = lane >> 4, t = lane & 15;
     const int row = 4 * (g >> 1) + (t >> 2);
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
       const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
       const int chunk = (col >> 3) ^ v_swz<D>(row);
-      v_off[cb] = row * D + chunk * 8 + (col & 7);
+      v_addr[cb] = smem_byte + 2 * C::TB + static_cast<uint32_t>(row * D + chunk * 8 + (col & 7)) * 2u;
     }
   }
-  __device__ static inline int k_swz_of(int r) { return iofa::k_swz<D>(r); }
 
-  // a3: S^T block scores of one tile from a K stage (raw dot products)
-  __device__ inline void scores(f32x16 (&s)[C::SB], const uint16_t* Ks) const {
+  // a3: scores S^T of one tile (raw dot products) from K stage S.
+  template <int S>
+  __device__ inline void scores(f32x16 (&s)[C::SB]) const {
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb) s[sb] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const int chunk = (2 * kk + hi) ^ k_swz;
 #pragma unroll
       for (int sb = 0; sb < C::SB; ++sb) {
-        const auto a = lds_vec8<T>(Ks + (32 * sb + k_row) * D + chunk * 8);
+        const auto a = __builtin_bit_cast(vec8, lds_read16(k_addr[kk] + S * C::TB + 32 * sb * D * 2));
         s[sb] = T::mfma(a, qf[kk], s[sb]);
       }
     }
   }
 
-  // a4 + a5: tile maximum, reference-maximum update, exponentials, row sum;
-  // returns P rounded to the input type as the B operand of KSTEPS products.
-  // Branch-free, so the scheduler can interleave it with independent MFMAs.
-  // TAIL masks keys at or beyond keys_valid to weight 0.
+  // a6: acc += P V for one tile from V stage S.  The A operand (V^T) comes
+  // from two transposed reads: keys 16*ks + 4*hi + 0..3 and
+  // 16*ks + 8 + 4*hi + 0..3, the keys the P registers hold in k-slots
+  // 8*hi + 0..3 and 8*hi + 4..7.
+  template <int S>
+  __device__ inline void pv(const vec8 (&pk)[C::KSTEPS]) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const uint32_t a0 = v_addr[cb] + S * C::TB + 16 * ks * D * 2;
+        const s16x4 lo = lds_read_tr8(a0);
+        const s16x4 up = lds_read_tr8(a0 + 8 * D * 2);
+        const auto a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[cb] = T::mfma(a, pk[ks], o[cb]);
+      }
+    }
+  }
+
+  // a4 + a5: tile maximum, reference-maximum update, exponentials, row sum,
+  // packing of P to the input type.  Returns the rescale factor of the older
+  // terms.  TAIL masks keys at or beyond keys_valid to weight 0.
   template <bool TAIL>
-  __device__ inline float softmax(f32x16 (&s)[C::SB], typename T::vec8 (&pk)[C::KSTEPS],
-                                  float c2, int keys_valid) {
+  __device__ inline float softmax(f32x16 (&s)[C::SB], vec8 (&pk)[C::KSTEPS], float c2,
+                                  int keys_valid) {
     float mraw = -__builtin_inff();
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
@@ -132,8 +164,6 @@ struct WaveState {
         rs += p;
       }
     }
-    rs = halfwave_sum(rs);
-    l_run = alpha * l_run + rs;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const f32x16& p = s[ks >> 1];
@@ -141,54 +171,65 @@ struct WaveState {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = T::pack(p[b + 2 * e], p[b + 2 * e + 1]);
-      pk[ks] = __builtin_bit_cast(typename T::vec8, w);
+      pk[ks] = __builtin_bit_cast(vec8, w);
     }
+    rs = halfwave_sum(rs);
+    l_run = alpha * l_run + rs;
     return alpha;
   }
 
-  // a6: acc = alpha * acc + P V_j.  The A operand (V^T) comes from two
-  // transposed reads: keys 16*ks + 4*hi + 0..3 and 16*ks + 8 + 4*hi + 0..3,
-  // the same keys the P registers hold in k-slots 0..3 and 4..7.
-  __device__ inline void accumulate(const typename T::vec8 (&pk)[C::KSTEPS], float alpha,
-                                    const uint16_t* Vs) {
+  __device__ inline void rescale(float alpha) {
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb) o[cb] *= alpha;
     }
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-        const uint16_t* p0 = Vs + v_off[cb] + (16 * ks) * D;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(IOFA_LDS(s16x4, p0));
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(IOFA_LDS(s16x4, p0 + 8 * D));
-        const auto a = __builtin_bit_cast(typename T::vec8,
-                                          __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[cb] = T::mfma(a, pk[ks], o[cb]);
-      }
-    }
   }
 };
 
-// Workgroup schedule with two K stages and two V stages in LDS.  While tile j
-// is processed (its scores were computed during tile j-1), the wave computes
-// the scores of tile j+1 from K stage (j+1)%2 -- independent work the
-// scheduler interleaves with tile j's softmax -- and multiplies P_j with V
-// stage j%2.  Direct global-to-LDS copies of K_{j+2} and V_{j+1} are issued
-// at the top of tile j into the two stages no wave reads during tile j
-// (K stage j%2, V stage (j+1)%2) and awaited before the one barrier per tile.
+// Interleave, inside one scheduling region, NMFMA matrix products with the
+// NDS LDS fragment reads they consume (LEAD reads first, the rest spread
+// evenly) and the vector work of a softmax (VPM instructions per product).
+template <int NMFMA, int R, int VPM, int I>
+__device__ inline void interleave_step() {
+  if constexpr (I < NMFMA) {
+    constexpr int nrd = (I + 1) * R / NMFMA - I * R / NMFMA;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    if constexpr (nrd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nrd, 0);   // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);       // VALU
+    interleave_step<NMFMA, R, VPM, I + 1>();
+  }
+}
+template <int NMFMA, int NDS, int LEAD, int VPM>
+__device__ inline void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);        // DS reads
+  interleave_step<NMFMA, NDS - LEAD, VPM, 0>();
+}
+
+// Per wave, tile t of the key sweep (NT tiles) is processed in three steps:
+// its scores in iteration t-1, its softmax in iteration t, its P V product
+// in iteration t+1.  K tile t lives in K stage t%2, copied in iteration t-2;
+// V tile t in V stage t%2, copied in iteration t.  Iteration j (P = j%2):
+//   top     direct copies K_{j+2} -> K stage P (last read in iteration j-1)
+//           and V_j -> V stage P (last read in iteration j-1);
+//   middle  softmax_j (VALU) interleaved with P_{j-1} V_{j-1} (V stage 1-P)
+//           and scores_{j+1} (K stage 1-P) on the MFMA unit;
+//   bottom  rescale of O if the reference maximum moved; wait for this
+//           iteration's copies; barrier.
 template <class T, int D, int BC>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int N, int num_qtiles, int num_wg, float scale) {
   using C = FusedCfg<D, BC>;
+  using vec8 = typename T::vec8;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::SMEM];
-  uint16_t* const kst[2] = {smem, smem + C::TILE};
-  uint16_t* const vst[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
+  const uint32_t sm = lds_address(smem);
+  const uint32_t kst[2] = {sm, sm + C::TB};
+  const uint32_t vst[2] = {sm + 2 * C::TB, sm + 3 * C::TB};
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
 
   const int L = xcd_logical_id(blockIdx.x, num_wg);
   const int bh = L / num_qtiles, qt = L % num_qtiles;
@@ -197,21 +238,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  // a2 prologue: K_0, V_0, K_1 copies in flight while Q is loaded
-  const int ntiles = (N + BC - 1) / BC;
+  const int NT = (N + BC - 1) / BC;   // key tiles
+  const bool ragged = (N % BC) != 0;
   TileCopy<D, BC, false> kcp;
   TileCopy<D, BC, true> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
+
+  // a2 prologue: K_0 and K_1 in flight while Q is loaded
   kcp.copy(Kh, 0, N, kst[0]);
-  vcp.copy(Vh, 0, N, vst[0]);
-  if (ntiles > 1) kcp.copy(Kh, BC, N, kst[1]);
+  kcp.copy(Kh, BC, N, kst[1]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
   // to the fp32 scores is c2 = |scale| * log2(e) >= 0.
   WaveState<T, D, BC> ws;
-  ws.init_lanes(lane);
+  ws.init_lanes(lane, sm);
   const int q = qt * C::BR + wave * 32 + (lane & 31);
   const uint32_t flip = scale < 0.f ? 0x80008000u : 0u;
 #pragma unroll
@@ -219,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     u32x4 w = u32x4{0u, 0u, 0u, 0u};
     if (q < N) w = *reinterpret_cast<const u32x4*>(Qh + static_cast<size_t>(q) * D + 16 * kk + 8 * ws.hi);
     w ^= flip;
-    ws.qf[kk] = __builtin_bit_cast(typename T::vec8, w);
+    ws.qf[kk] = __builtin_bit_cast(vec8, w);
   }
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) ws.o[cb] = f32x16{};
@@ -230,40 +272,68 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa[C::SB], sb[C::SB];
-  ws.scores(sa, kst[0]);
-  __syncthreads();   // K stage 0 is refilled during tile 0
+  vec8 pa[C::KSTEPS], pb[C::KSTEPS];
+  ws.template scores<0>(sa);
+  __syncthreads();   // K stage 0 is refilled in iteration 0
 
-  // One tile: softmax of tile j interleaved with the scores of tile j+1
-  // (from K stage (j+1)%2; on the last tile these read a stale stage and are
-  // discarded), then P_j V_j.
-  auto tile = [&](int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB]) {
-    const int k0 = j * BC;
-    if (j + 2 < ntiles) kcp.copy(Kh, k0 + 2 * BC, N, kst[j & 1]);
-    if (j + 1 < ntiles) vcp.copy(Vh, k0 + BC, N, vst[(j + 1) & 1]);
-    typename T::vec8 pk[C::KSTEPS];
-    float alpha;
-    if (k0 + BC <= N) {
-      alpha = ws.template softmax<false>(s_cur, pk, c2, BC);
-      ws.scores(s_nxt, kst[(j + 1) & 1]);
-      // interleave: per score MFMA, its K fragment read and a slice of the
-      // softmax's vector work
-#pragma unroll
-      for (int i = 0; i < D / 16 * C::SB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
-      }
-    } else {
-      alpha = ws.template softmax<true>(s_cur, pk, c2, N - k0);
-      ws.scores(s_nxt, kst[(j + 1) & 1]);
-    }
-    ws.accumulate(pk, alpha, vst[j & 1]);
+  constexpr int NM = 2 * (D / 16) * C::SB;          // products per iteration
+  constexpr int NRD = (D / 16) * C::SB + 2 * NM / 2;  // K reads + 2 per P V product
+  auto bottom = [&](float alpha) {
+    ws.rescale(alpha);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile(j, sa, sb);
-    if (j + 1 < ntiles) tile(j + 1, sb, sa);
+  // one full iteration j with parity P (compile-time)
+  auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
+                       vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
+    constexpr int P = decltype(par)::value;
+    kcp.copy(Kh, (j + 2) * BC, N, kst[P]);
+    vcp.copy(Vh, j * BC, N, vst[P]);
+    const float alpha = ws.template softmax<false>(s_cur, p_cur, c2, BC);
+    ws.template pv<1 - P>(p_prev);
+    ws.template scores<1 - P>(s_nxt);
+    interleave_mfma_valu<NM, NRD, 4, 4>();
+    bottom(alpha);
+  };
+  // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
+  auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
+                  vec8 (&p_cur)[C::KSTEPS]) {
+    constexpr int P = decltype(par)::value;
+    vcp.copy(Vh, j * BC, N, vst[P]);
+    const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, N - j * BC)
+                               : ws.template softmax<false>(s_cur, p_cur, c2, BC);
+    if (j > 0) ws.template pv<1 - P>(p_prev);
+    bottom(alpha);
+    ws.template pv<P>(p_cur);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  if (NT == 1) {
+    last(P0{}, 0, sa, pb, pa);
+  } else {
+    // iteration 0: softmax_0 with scores_1
+    kcp.copy(Kh, 2 * BC, N, kst[0]);
+    vcp.copy(Vh, 0, N, vst[0]);
+    {
+      const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
+      ws.template scores<1>(sb);
+      constexpr int NS1 = (D / 16) * C::SB;
+      interleave_mfma_valu<NS1, NS1, 2, 4>();
+      bottom(alpha);
+    }
+    // iterations 1 .. NT-2, two per trip so register sets and stages alternate
+    int j = 1;
+    for (; j + 1 < NT - 1; j += 2) {
+      iteration(P1{}, j, sb, sa, pa, pb);
+      iteration(P0{}, j + 1, sa, sb, pb, pa);
+    }
+    if (j < NT - 1) {
+      iteration(P1{}, j, sb, sa, pa, pb);
+      last(P0{}, j + 1, sa, pb, pa);
+    } else {
+      last(P1{}, j, sb, pa, pb);
+    }
   }
 
   // a7: O = acc / l rounded to the input type; LSE = ln2 * (m + log2 l)
@@ -375,7 +445,12 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
 
 // ------------------------------------------------------------- launchers
 
-template <class T, int D, int BC = 64>
+// Keys per tile: 32 at d = 128 (keeps the three-stage pipeline's registers
+// within the 256 a wave has at two waves per SIMD), 64 at d = 64.
+template <int D>
+constexpr int kFusedBC = D == 128 ? 32 : 64;
+
+template <class T, int D, int BC = kFusedBC<D>>
 static hipError_t launch16(const FwdArgs& a) {
   using C = FusedCfg<D, BC>;
   const int qtiles = static_cast<int>((a.N + C::BR - 1) / C::BR);
@@ -399,7 +474,7 @@ static hipError_t launch32(const FwdArgs& a) {
 }
 
 int64_t fused_workgroups(int dtype, int64_t BH, int64_t N) {
-  const int64_t br = (dtype == kDtypeF32) ? 32 : FusedCfg<128, 64>::BR;
+  const int64_t br = (dtype == kDtypeF32) ? 32 : FusedCfg<128, kFusedBC<128>>::BR;
   return BH * ((N + br - 1) / br);
 }
 
