@@ -52,6 +52,14 @@ struct FusedCfg {
 // maximum bounds every exponential by 2^8, and the O accumulator is then
 // rescaled only on the (rare, wave-uniform) tiles that move m.
 constexpr float kRescaleSlack = 8.0f;
+// Largest partial row sum (per lane, per tile) accepted without moving the
+// reference maximum.  It bounds every unnormalised weight, which is rounded
+// to the input type for the P V product: 2^32 for bf16 (range of fp32),
+// 2^15 for fp16 (largest finite value 65504).
+template <class T>
+constexpr float kLazyBound = 4294967296.0f;
+template <>
+constexpr float kLazyBound<F16> = 32768.0f;
 
 // One wave's share of the online-softmax recurrence.
 template <class T, int D, int BC>
@@ -178,6 +186,49 @@ struct WaveState {
     return alpha;
   }
 
+  // a5 without a4 (the usual case after the first tile): exponentials
+  // against the current reference maximum, packing, and this lane's partial
+  // row sum, which is returned.  s is left intact.  Every exponential is at
+  // most the partial sum, so when the sum is at most kLazyBound on all lanes
+  // (commit_lazy), every term fits the packed type, the accumulators stay far
+  // from overflow, and the reference need not move; otherwise (a score above
+  // the reference by more than log2 kLazyBound, or the -inf reference of an
+  // empty state) the tile is redone with its maximum by softmax<false>.  A
+  // failed check implies a tile maximum more than kRescaleSlack above the
+  // reference (at most 32 terms of 2^kRescaleSlack per lane stay below both
+  // bounds), so the redo always moves the reference.
+  __device__ inline float softmax_lazy(const f32x16 (&s)[C::SB], vec8 (&pk)[C::KSTEPS],
+                                       float c2) const {
+    const float msub = m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const f32x16& v = s[ks >> 1];
+      const int b = 8 * (ks & 1);
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(v[b + 2 * e], c2, -msub));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(v[b + 2 * e + 1], c2, -msub));
+        rs += p0;
+        rs += p1;
+        w[e] = T::pack(p0, p1);
+      }
+      pk[ks] = __builtin_bit_cast(vec8, w);
+    }
+    return rs;
+  }
+  // Accept a lazy tile (returns 1) or redo it with its maximum (returns the
+  // rescale factor of the older terms).
+  __device__ inline float commit_lazy(float rs, f32x16 (&s)[C::SB], vec8 (&pk)[C::KSTEPS],
+                                      float c2) {
+    if (__all(rs <= kLazyBound<T>)) {
+      l_run += halfwave_sum(rs);
+      return 1.f;
+    }
+    return softmax<false>(s, pk, c2, BC);
+  }
+
   __device__ inline void rescale(float alpha) {
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -289,11 +340,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     constexpr int P = decltype(par)::value;
     kcp.copy(Kh, (j + 2) * BC, N, kst[P]);
     vcp.copy(Vh, j * BC, N, vst[P]);
-    const float alpha = ws.template softmax<false>(s_cur, p_cur, c2, BC);
+    const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv<1 - P>(p_prev);
     ws.template scores<1 - P>(s_nxt);
     interleave_mfma_valu<NM, NRD, 4, 4>();
-    bottom(alpha);
+    bottom(ws.commit_lazy(rs, s_cur, p_cur, c2));
   };
   // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],

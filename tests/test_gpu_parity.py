@@ -119,8 +119,12 @@ def test_shift_invariance_on_gpu(dev):
     shift = np.float32(scale) * (widen(q) @ u.double().numpy())
     dl = l2.double().numpy() - l1.double().numpy()
     assert np.abs(dl - shift).max() <= 2e-3 * max(1.0, np.abs(shift).max())
-    max_abs, rel_f, _ = errors(o2, None, widen(o1), None)
-    assert max_abs <= 1e-2 and rel_f <= 5e-3
+    # two outputs rounded independently to bf16 may differ by one unit in the
+    # last place of |O| (2u|O|, u = 2^-8) on top of the fused bar
+    o1w, o2w = widen(o1), widen(o2)
+    excess = np.abs(o2w - o1w) - 2.0 * 2.0 ** -8 * np.abs(o1w)
+    rel_f = np.linalg.norm(o2w - o1w) / np.linalg.norm(o1w)
+    assert excess.max() <= 1e-2 and rel_f <= 5e-3
 
 
 def test_deterministic(dev):
