@@ -249,17 +249,19 @@ __device__ inline void wait_vmem() {
 
 // Per-lane part of the direct copies of one K or V tile (BC rows x D 16-bit
 // elements, row-major, chunks swizzled as above) from global memory into an
-// LDS stage.  Wave w writes the 1 KiB blocks b = w + 4*i (i = 0 ..
-// PER_WAVE-1); with this interleave the swizzle of every row a lane copies
-// is the same, and lane offsets differ between blocks only by a constant.
-template <int D, int BC, bool IS_V>
+// LDS stage by the NWV waves of a workgroup.  Wave w writes the 1 KiB blocks
+// b = w + NWV*i (i = 0 .. PER_WAVE-1); with this interleave the swizzle of
+// every row a lane copies is the same, and lane offsets differ between
+// blocks only by a constant.
+template <int D, int BC, bool IS_V, int NWV = 4>
 struct TileCopy {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_BLK = 64 / CH;     // rows in one 1 KiB block
   static constexpr int BLKS = BC * D * 2 / 1024;   // 1 KiB blocks per tile
-  static constexpr int PER_WAVE = BLKS / 4;
-  static constexpr int ROW_STEP = 4 * ROWS_PER_BLK;  // rows between a lane's blocks
-  static_assert(PER_WAVE * 4 == BLKS, "tile must split over 4 waves");
+  static constexpr int PER_WAVE = BLKS / NWV;
+  static constexpr int ROW_STEP = NWV * ROWS_PER_BLK;  // rows between a lane's blocks
+  static_assert(PER_WAVE * NWV == BLKS, "tile must split over the waves");
+  static_assert(ROW_STEP % 16 == 0, "blocks of one lane must share a swizzle");
   uint32_t voff0;     // byte offset of this lane's chunk in block i = 0
   uint32_t lds_wave;  // byte offset of block i = 0 inside a stage (wave-uniform)
 
@@ -281,7 +283,7 @@ struct TileCopy {
                                   static_cast<uint32_t>(rows) * (D * 2u));
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
-      lds_dma16(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * 4096u);
+      lds_dma16(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * (NWV * 1024u));
   }
 };
 
