@@ -55,6 +55,11 @@ def parse():
                         "into the kernel-trace summary under profiles/ and exit")
     p.add_argument("--trace-cmd", default="",
                    help="the bench.py arguments of that run (recorded in the summary)")
+    p.add_argument("--sq-from", metavar="PMC_DIR",
+                   help="summarise a `rocprofv3 --pmc` run of bench.py with SQ_BUSY_CYCLES, "
+                        "SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_INSTS_LDS, "
+                        "SQ_INSTS_VALU_TRANS_F32 and SQ_WAVES into the shader-counter summary "
+                        "under profiles/ (effective clock, MFMA busy fraction) and exit")
     p.add_argument("--copy-mib", type=int, default=1024,
                    help="size of the calibration copy in those runs")
     return p.parse_args()
@@ -239,6 +244,84 @@ def summarise_trace(trace_dir, index, spec, bench_args):
     print(path)
 
 
+SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES"]
+SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
+SIMDS = 1024                 # 256 CUs x 4
+
+
+def summarise_sq(pmc_dir, index, spec):
+    """Effective shader clock and MFMA busy fraction of the fused kernel.
+
+    SQ_BUSY_CYCLES counts, per shader engine, the cycles any wave is
+    resident; summed over the 32 engines and divided by 32 it is the
+    kernel's length in shader cycles, so dividing by the dispatch's duration
+    gives the clock it ran at.  SQ_VALU_MFMA_BUSY_CYCLES summed over the
+    SIMDs, over SIMDs x kernel cycles, is the fraction of time the matrix
+    cores were busy."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    per = {}
+    for f in files:
+        with open(f, encoding="utf-8") as fh:
+            for r in csv.DictReader(fh):
+                if FUSED_KERNEL_NAME not in r["Kernel_Name"]:
+                    continue
+                d = per.setdefault(int(r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit("no fused-kernel dispatches in the counter run")
+    keys = sorted(per)
+    avg = {c: sum(per[k][c] for k in keys) / len(keys) for c in SQ_COUNTERS + ["ns"]}
+    cycles = avg["SQ_BUSY_CYCLES"] / SHADER_ENGINES
+    mhz = cycles / (avg["ns"] * 1e-3)
+    mfma_busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
+    flops = 4.0 * spec["B"] * spec["H"] * spec["N"] ** 2 * spec["d"]
+    tflops = flops / (avg["ns"] * 1e-9) / 1e12
+    peak_at_clock = PEAK_BF16_TFLOPS * mhz / 2400.0
+    waves = avg["SQ_WAVES"]
+    mfma = avg["SQ_INSTS_MFMA"]
+    lines = [
+        f"# Shader counters of the fused forward, {spec['name']}",
+        "",
+        "Command (one MI355X, from the repository root):",
+        "",
+        "```",
+        f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {pmc_dir} -o run --output-format csv -- "
+        f"python bench.py --workload {index} --steps 3 --warmup 1 --no-naive --no-cpu-baseline",
+        f"python bench.py --workload {index} --sq-from {pmc_dir}",
+        "```",
+        "",
+        f"Averages over {len(keys)} dispatches of the fused kernel:",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| dispatch duration | {avg['ns'] / 1e3:.1f} us ({tflops:.1f} TFLOP/s at 4BHN^2d) |",
+        f"| SQ_BUSY_CYCLES / 32 engines | {cycles:.0f} shader cycles |",
+        f"| effective shader clock | {mhz:.0f} MHz (nominal peak clock 2400 MHz) |",
+        f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / cycles) | {mfma_busy:.3f} |",
+        f"| dense bf16 MFMA peak at that clock | {peak_at_clock:.0f} TFLOP/s "
+        f"(achieved / that = {tflops / peak_at_clock:.3f}) |",
+        f"| waves | {waves:.0f} |",
+        f"| per wave: MFMA / VALU (incl. MFMA) / transcendental / LDS instructions | "
+        f"{mfma / waves:.0f} / {avg['SQ_INSTS_VALU'] / waves:.0f} / "
+        f"{avg['SQ_INSTS_VALU_TRANS_F32'] / waves:.0f} / {avg['SQ_INSTS_LDS'] / waves:.0f} |",
+        f"| non-MFMA VALU + LDS instructions per MFMA | "
+        f"{(avg['SQ_INSTS_VALU'] - mfma + avg['SQ_INSTS_LDS']) / mfma:.2f} |",
+        "",
+        f"kernel_sources_sha256_16: {sources_hash()}",
+        "",
+    ]
+    path = os.path.join(ROOT, f"profiles/sq_counters_fused_fwd_{workload_tag(spec)}.md")
+    with open(path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    print(path)
+
+
 def read_traffic(spec):
     """bytes_per_launch from the committed traffic summary, or None when it is
     missing or was taken on other kernel sources."""
@@ -325,6 +408,10 @@ def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
 
 def main():
     args = parse()
+    if args.sq_from:
+        from workloads import WORKLOADS
+        summarise_sq(args.sq_from, args.workload, WORKLOADS[args.workload])
+        return
     if args.trace_from:
         from workloads import WORKLOADS
         summarise_trace(args.trace_from, args.workload, WORKLOADS[args.workload], args.trace_cmd)
