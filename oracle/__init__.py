@@ -11,7 +11,8 @@ Pages cited (titles/sections as printed on them):
   [ctyun]  ctyun.cn developer article on FlashAttention -- sections
            "背景 / Transformer的复杂度", "核心思想", "MAC分析".
   [jiahao] "Flash Attention" note on special-jiahao.github.io -- sections
-           "Standard Attention", "增量求解 softmax".
+           "Standard Attention", "增量求解 softmax" (also the block merge
+           of partial attention results, merge.py).
   [xinc]   xinc.fun archive 235 -- sections "6. 标准注意力为什么慢",
            "7. Online Softmax".
 
@@ -36,6 +37,7 @@ from .softmax import (
 )
 from .tiled import tiled_online_attention
 from .mac_count import standard_attention_mac
+from .merge import merge_partials, partial_attention
 
 __all__ = [
     "decode_bf16",
@@ -48,4 +50,6 @@ __all__ = [
     "online_softmax_output",
     "tiled_online_attention",
     "standard_attention_mac",
+    "partial_attention",
+    "merge_partials",
 ]

@@ -416,3 +416,87 @@ def test_planted_mistakes_fail_a_pin(kind, monkeypatch):
     held = guarded(lambda: brute_force_pin_holds(_oracle_one_head, cases)) and \
         guarded(lambda: closed_form_pin_holds(_oracle_one_head))
     assert not held, f"mutant {kind!r} passed every pin"
+
+
+# ------------------------------------------------ partial attention + merge
+
+def _random_head(seed, B=1, H=2, N=37, d=8, dv=5):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d)),
+            rng.standard_normal((B, H, N, dv)))
+
+
+@pytest.mark.parametrize("cuts", [[0, 37], [0, 1, 37], [0, 16, 32, 37], [0, 5, 6, 20, 36, 37],
+                                  list(range(0, 38))])
+def test_merge_of_key_blocks_equals_definition(cuts):
+    # [jiahao] "增量求解 softmax": the blockwise merge reproduces the global
+    # softmax; here for attention rows with keys cut at `cuts`
+    q, k, v = _random_head(3)
+    scale = 0.7
+    parts = [oracle.partial_attention(q, k, v, scale, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = oracle.merge_partials(np.stack([p[0] for p in parts]),
+                                   np.stack([p[1] for p in parts]))
+    o_ref, lse_ref = oracle.standard_attention(q, k, v, scale)
+    assert np.abs(o - o_ref).max() <= 1e-13
+    assert np.abs(lse - lse_ref).max() <= 1e-13
+
+
+def test_partial_attention_over_all_keys_is_the_definition():
+    q, k, v = _random_head(4)
+    o, lse = oracle.partial_attention(q, k, v, 0.3, 0, 37)
+    o_ref, lse_ref = oracle.standard_attention(q, k, v, 0.3)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+
+
+def test_merge_identities():
+    q, k, v = _random_head(5)
+    a = oracle.partial_attention(q, k, v, 0.5, 0, 20)
+    b = oracle.partial_attention(q, k, v, 0.5, 20, 37)
+    empty = oracle.partial_attention(q, k, v, 0.5, 7, 7)
+    assert np.all(empty[1] == -np.inf) and np.all(empty[0] == 0)
+    one = oracle.merge_partials(a[0][None], a[1][None])           # G = 1
+    assert np.abs(one[0] - a[0]).max() <= 1e-15 and np.abs(one[1] - a[1]).max() <= 1e-15
+    ab = oracle.merge_partials(np.stack([a[0], b[0]]), np.stack([a[1], b[1]]))
+    ba = oracle.merge_partials(np.stack([b[0], a[0]]), np.stack([b[1], a[1]]))
+    aeb = oracle.merge_partials(np.stack([a[0], empty[0], b[0]]),
+                                np.stack([a[1], empty[1], b[1]]))
+    for other in (ba, aeb):
+        assert np.abs(other[0] - ab[0]).max() <= 1e-14
+        assert np.abs(other[1] - ab[1]).max() <= 1e-14
+
+
+@pytest.mark.parametrize("n", [2, 5, 16])
+def test_merge_weights_match_two_block_softmax(n):
+    # one query row, V = identity: the output row is the attention weights, so
+    # the merge must give the same vector as the two-block formula of
+    # [jiahao] "增量求解 softmax" for every split point
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n) * 3
+    q = np.ones((1, 1, 1, 1))
+    kk = x.reshape(1, 1, n, 1)                 # scores = x with scale 1
+    v = np.eye(n).reshape(1, 1, n, n)
+    for cut in range(n + 1):
+        a = oracle.partial_attention(q, kk, v, 1.0, 0, cut)
+        b = oracle.partial_attention(q, kk, v, 1.0, cut, n)
+        o, lse = oracle.merge_partials(np.stack([a[0], b[0]]), np.stack([a[1], b[1]]))
+        s_glob, m, l, _ = oracle.two_block_softmax(x, cut)
+        assert np.abs(o[0, 0, 0] - s_glob).max() <= 1e-14
+        assert abs(lse[0, 0, 0] - (m + np.log(l))) <= 1e-13
+
+
+@pytest.mark.parametrize("kind", ["unnormalised", "max_not_lse", "equal_weights"])
+def test_planted_merge_mistakes_fail_a_pin(kind):
+    def bad_merge(o_parts, lse_parts):
+        if kind == "unnormalised":
+            w = np.exp(lse_parts)
+            return (w[..., None] * o_parts).sum(axis=0), np.log(w.sum(axis=0))
+        if kind == "max_not_lse":
+            lse = lse_parts.max(axis=0)
+            w = np.exp(lse_parts - lse)
+            return (w[..., None] * o_parts).sum(axis=0), lse
+        return o_parts.mean(axis=0), np.log(np.exp(lse_parts).sum(axis=0))
+    q, k, v = _random_head(9)
+    parts = [oracle.partial_attention(q, k, v, 0.7, a, b) for a, b in ((0, 10), (10, 37))]
+    o, lse = bad_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    o_ref, lse_ref = oracle.standard_attention(q, k, v, 0.7)
+    assert np.abs(o - o_ref).max() > 1e-6 or np.abs(lse - lse_ref).max() > 1e-6
