@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--no-naive", action="store_true", help="skip the naive contrast")
+    p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -406,6 +407,49 @@ def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
     }
 
 
+def splitkv_contrast(spec, args, torch, iofa, dev):
+    """One GPU's share of the workload when its heads are split over 8 GPUs
+    (H/8 heads): few query-tile workgroups, so the key sweep is split into
+    ranges and merged.  Times the fused kernel alone, the split-KV path
+    (partial pass + merge) and the merge kernel alone (HBM-bound: it reads
+    G*(d+1) and writes d elements + 1 fp32 LSE per row)."""
+    from workloads import make_qkv
+    B, H, N, d = spec["B"], max(1, spec["H"] // 8), spec["N"], spec["d"]
+    q, k, v = (t.to(dev) for t in make_qkv(B, H, N, d, spec["dtype"], seed_base=4242))
+    scale = iofa.default_scale(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    g = iofa.fa_splitkv_num_splits(B, H, N, d, q.dtype, 0)
+    ws = torch.empty(max(16, iofa.fa_splitkv_workspace_bytes(B, H, N, d, q.dtype, g)),
+                     dtype=torch.uint8, device=dev)
+    flops = 4.0 * B * H * N * N * d
+    steps = max(5, min(args.steps, 30))
+    _, f_ms = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch)
+    _, s_ms = time_launches(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g),
+                            steps, 3, torch)
+    rows = B * H * N
+    flat = ws.view(torch.float32)
+    o_part = flat[:g * rows * d].view(g, rows, d)
+    lse_part = flat[g * rows * d:g * rows * (d + 1)].view(g, rows)
+    o2 = torch.empty((rows, d), dtype=q.dtype, device=dev)
+    l2 = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _, m_ms = time_launches(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2),
+                            steps, 3, torch)
+    merge_bytes = g * rows * (d + 1) * 4 + rows * (d * q.element_size() + 4)
+    return {
+        "workload": f"{spec['dtype']} B{B} H{H} N{N} d{d} (one GPU's share of an 8-way head split)",
+        "num_splits": g,
+        "fused_ms": round(f_ms, 4), "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1),
+        "splitkv_ms": round(s_ms, 4), "splitkv_tflops": round(flops / (s_ms * 1e-3) / 1e12, 1),
+        "speedup_splitkv_over_fused": round(f_ms / s_ms, 3),
+        "merge_ms": round(m_ms, 4),
+        "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / (m_ms * 1e-3) / 1e9, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(merge_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                           "bytes_per_launch": merge_bytes},
+    }
+
+
 def main():
     args = parse()
     if args.sq_from:
@@ -515,6 +559,10 @@ def main():
             }
             del s_ws, p_ws
             print(f"[bench] naive: {n_ev:.4f} ms/call", file=sys.stderr, flush=True)
+
+    if not args.no_splitkv and spec["dtype"] != "fp32":
+        line["splitkv_contrast"] = splitkv_contrast(spec, args, torch, iofa, dev)
+        print(f"[bench] split-KV: {line['splitkv_contrast']}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)

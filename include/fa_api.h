@@ -112,6 +112,65 @@ int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O,
                  float* LSE, void* S_ws, void* P_ws, int64_t B, int64_t H,
                  int64_t N, int64_t d, float scale, int dtype, void* stream);
 
+/*
+ * Split-KV forward: the same result as fa_fwd, computed in two passes so
+ * that problems with few query tiles (small B * H * N) still fill the chip.
+ *   pass 1  the keys are cut into G contiguous ranges of whole key tiles;
+ *           every (head, key range, query tile) is one workgroup of the
+ *           fused kernel, writing its normalised partial output O_g (fp32)
+ *           and log-sum-exp LSE_g for its range only;
+ *   pass 2  fa_merge_partials' kernel combines the G partials per row.
+ * The combination is the block merge of the special-jiahao.github.io
+ * "Flash Attention" note, section "增量求解 softmax" (the global softmax
+ * from the blocks' local ones), for G blocks: LSE = ln sum_g e^{LSE_g},
+ * O = sum_g e^{LSE_g - LSE} O_g.
+ *
+ *   num_splits  G requested; 0 (or less) chooses G so that pass 1 has about
+ *               512 workgroups; G is clamped to [1, min(64, key tiles)].
+ *               With G = 1 the call is fa_fwd and the workspace is unused.
+ *   workspace   caller-owned device memory of at least
+ *               fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits)
+ *               bytes, 16-byte aligned, not overlapping any argument; may be
+ *               NULL when that size is 0.  Contents on return: the partials
+ *               (G x B*H*N*d fp32 outputs, then G x B*H*N fp32 LSEs).
+ *   workspace_bytes  its size; a smaller size than needed is FA_ERR_SHAPE.
+ * Other arguments, layouts and errors as fa_fwd.
+ */
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   void* workspace, size_t workspace_bytes, int num_splits, int64_t B,
+                   int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream);
+
+/* The G that fa_fwd_splitkv uses for `requested` (see above); 0 for invalid
+ * sizes or dtype. */
+int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested);
+
+/* Workspace bytes fa_fwd_splitkv needs: G * B*H*N * (d + 1) * 4 for the G it
+ * resolves, 0 when G = 1 or for invalid arguments. */
+size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                                  int num_splits);
+
+/*
+ * Merge of num_parts partial attention results over disjoint key sets (the
+ * block merge of the special-jiahao.github.io "Flash Attention" note,
+ * section "增量求解 softmax", for num_parts blocks), per row r:
+ *     LSE[r] = ln sum_g e^{LSE_part[g][r]}
+ *     O[r]   = sum_g e^{LSE_part[g][r] - LSE[r]} O_part[g][r]
+ * It is the combining step of fa_fwd_splitkv, and the step a caller would
+ * run after gathering per-device partials of a key-sharded attention.
+ *   O_part    in:  (num_parts, rows, d) fp32, each row normalised by its own
+ *                  block's denominator; 16-byte aligned.
+ *   LSE_part  in:  (num_parts, rows) fp32 natural-log log-sum-exps; -inf
+ *                  marks a block without keys (its O_part row is ignored
+ *                  but must be finite); 4-byte aligned.
+ *   O         out: (rows, d) in `dtype` (RNE), 16-byte aligned.
+ *   LSE       out: (rows) fp32, 4-byte aligned; -inf (and O = 0) for a row
+ *                  whose blocks are all empty.
+ *   num_parts 1 .. 4096; rows >= 0 (0: nothing is enqueued); d in {64, 128}.
+ * Outputs must not overlap inputs.  Errors as fa_fwd.
+ */
+int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts, int64_t rows,
+                      int64_t d, void* O, float* LSE, int dtype, void* stream);
+
 /* Bytes of ONE naive workspace (S or P): B * H * N * ldS * sizeof(dtype),
  * ldS = N rounded up to a multiple of 8.  Returns 0 for an invalid dtype
  * or negative sizes. */

@@ -1,14 +1,17 @@
 """Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
 
-The functions ``fa_fwd``, ``fa_naive_fwd``, ``fa_naive_workspace_bytes``,
-``fa_status_string``, ``fa_last_error`` and ``fa_version`` carry the names
+The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_splitkv_num_splits``,
+``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_naive_fwd``,
+``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
+``fa_version`` carry the names
 and meaning of the entry points declared in ``include/fa_api.h``; they only
 marshal torch tensors into pointers, sizes and the current HIP stream.  Every
 step of the computation runs in the HIP kernels of ``libiofa.so``; there is
 no CPU fallback, and a missing library raises instead of computing.
 
-``forward`` and ``naive_forward`` are conveniences that allocate the outputs
-(and the naive path's workspaces) with torch and call the entry points.
+``forward``, ``forward_splitkv`` and ``naive_forward`` are conveniences
+that allocate the outputs (and workspaces) with torch and call the entry
+points.
 """
 
 import ctypes
@@ -20,8 +23,10 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
-    "fa_fwd", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
-    "fa_last_error", "fa_version", "forward", "naive_forward", "default_scale",
+    "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
+    "fa_merge_partials", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
+    "fa_last_error", "fa_version", "forward", "forward_splitkv", "naive_forward",
+    "default_scale",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -58,6 +63,15 @@ def load_library():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, fp, vp, ctypes.c_size_t, ctypes.c_int,
+                                   i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_splitkv_num_splits.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_splitkv_num_splits.restype = ctypes.c_int
+    lib.fa_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_merge_partials.argtypes = [fp, fp, ctypes.c_int, i64, i64, vp, fp, ctypes.c_int, vp]
+    lib.fa_merge_partials.restype = ctypes.c_int
     lib.fa_naive_fwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, i64, i64, i64, i64,
                                  ctypes.c_float, ctypes.c_int, vp]
     lib.fa_naive_fwd.restype = ctypes.c_int
@@ -124,6 +138,55 @@ def fa_fwd(q, k, v, o, lse, scale, stream=None):
     _check(st)
 
 
+def fa_fwd_splitkv(q, k, v, o, lse, workspace, scale, num_splits=0, stream=None):
+    """Split-KV forward; workspace is a byte (uint8) tensor of at least
+    fa_splitkv_workspace_bytes() bytes (may be None when that is 0)."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous fp32 (B, H, N) tensor")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), _ptr(workspace),
+                                ws_bytes, int(num_splits), B, H, N, d, float(scale),
+                                _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+def fa_splitkv_num_splits(B, H, N, d, dtype, requested=0):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_splitkv_num_splits(B, H, N, d, code, int(requested)))
+
+
+def fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits=0):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_splitkv_workspace_bytes(B, H, N, d, code, int(num_splits)))
+
+
+def fa_merge_partials(o_part, lse_part, o, lse, stream=None):
+    """Merge partials: o_part (G, rows, d) fp32, lse_part (G, rows) fp32 into
+    o (rows, d) and lse (rows) fp32; o's dtype selects the output type."""
+    lib = load_library()
+    if o_part.dim() != 3 or lse_part.dim() != 2:
+        raise ValueError("o_part must be (G, rows, d) and lse_part (G, rows)")
+    G, rows, d = (int(x) for x in o_part.shape)
+    for name, t, dt in (("o_part", o_part, torch.float32), ("lse_part", lse_part, torch.float32),
+                        ("lse", lse, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor")
+    if tuple(lse_part.shape) != (G, rows) or tuple(o.shape) != (rows, d) \
+            or tuple(lse.shape) != (rows,) or not o.is_contiguous():
+        raise ValueError("shapes must be o_part (G, rows, d), lse_part (G, rows), "
+                         "o (rows, d), lse (rows,)")
+    if o.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {o.dtype}")
+    with torch.cuda.device(o.device):
+        st = lib.fa_merge_partials(_fptr(o_part), _fptr(lse_part), G, rows, d, _ptr(o),
+                                   _fptr(lse), _DTYPE_CODE[o.dtype], _stream(stream, o.device))
+    _check(st)
+
+
 def fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream=None):
     """Naive three-kernel forward; s_ws and p_ws are byte (uint8) tensors of
     fa_naive_workspace_bytes() bytes each; lse may be None."""
@@ -171,6 +234,19 @@ def forward(q, k, v, scale=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale, stream)
+    return o, lse
+
+
+def forward_splitkv(q, k, v, scale=None, num_splits=0, stream=None):
+    """Allocate O, LSE and the workspace and run the split-KV forward.
+    Returns (o, lse)."""
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    nbytes = fa_splitkv_workspace_bytes(B, H, N, d, q.dtype, num_splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+    fa_fwd_splitkv(q, k, v, o, lse, ws, scale, num_splits, stream)
     return o, lse
 
 

@@ -38,6 +38,12 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t round_up8(int64_t n) { return (n + 7) / 8 * 8; }
 
+// Split-KV policy: at most this many key ranges, and enough of them that the
+// partial pass has about this many workgroups (two per CU on 256 CUs).
+constexpr int64_t kMaxSplits = 64;
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int kMaxMergeParts = 4096;
+
 struct Region {
   const void* p;
   size_t bytes;
@@ -107,10 +113,98 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   const Region out[2] = {{O, tensor, "O"}, {LSE, lse, "LSE"}};
   st = check_aliasing(in, 3, out, 2);
   if (st != FA_OK) return st;
-  if (iofa::fused_workgroups(dtype, B * H, N) >= (int64_t(1) << 31))
+  if (iofa::fused_workgroups(dtype, B * H, N, 1) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
   iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
   return hip_status(iofa::launch_fused(a), "fused forward launch");
+}
+
+int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested) {
+  if (elem_bytes(dtype) == 0 || B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const int64_t tiles = (N + iofa::fused_key_tile(dtype, d) - 1) / iofa::fused_key_tile(dtype, d);
+  const int64_t cap = tiles < kMaxSplits ? tiles : kMaxSplits;
+  int64_t g = requested;
+  if (g <= 0) {
+    // enough workgroups for one full round at two per CU on 256 CUs
+    const int64_t per_split = iofa::fused_workgroups(dtype, B * H, N, 1);
+    g = (kTargetWorkgroups + per_split - 1) / per_split;
+  }
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                                  int num_splits) {
+  const int g = fa_splitkv_num_splits(B, H, N, d, dtype, num_splits);
+  if (g <= 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N);
+  return static_cast<size_t>(g) * rows * (static_cast<size_t>(d) + 1) * sizeof(float);
+}
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   void* workspace, size_t workspace_bytes, int num_splits, int64_t B, int64_t H,
+                   int64_t N, int64_t d, float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  bool empty = false;
+  int st = check_common(Q, K, V, O, LSE, true, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  const int g = fa_splitkv_num_splits(B, H, N, d, dtype, num_splits);
+  const size_t tensor = static_cast<size_t>(B * H * N * d) * elem_bytes(dtype);
+  const size_t lse = static_cast<size_t>(B * H * N) * sizeof(float);
+  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits);
+  if (g > 1) {
+    if (!workspace) return fail(FA_ERR_NULL, "workspace must not be NULL when splitting");
+    if (!aligned(workspace, 16)) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_SHAPE, "workspace holds " + std::to_string(workspace_bytes) +
+                                    " bytes, the split needs " + std::to_string(need));
+  }
+  const Region in[3] = {{Q, tensor, "Q"}, {K, tensor, "K"}, {V, tensor, "V"}};
+  const Region out[3] = {{O, tensor, "O"}, {LSE, lse, "LSE"},
+                         {workspace, g > 1 ? need : 0, "workspace"}};
+  st = check_aliasing(in, 3, out, 3);
+  if (st != FA_OK) return st;
+  if (iofa::fused_workgroups(dtype, B * H, N, g) >= (int64_t(1) << 31) ||
+      iofa::merge_workgroups(B * H * N, d) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
+  if (g == 1) return hip_status(iofa::launch_fused(a), "fused forward launch");
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = o_part + static_cast<size_t>(g) * B * H * N * d;
+  st = hip_status(iofa::launch_fused_partial(a, g, o_part, lse_part), "split-KV partial launch");
+  if (st != FA_OK) return st;
+  iofa::MergeArgs m{o_part, lse_part, g, B * H * N, d, O, LSE, dtype,
+                    static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_merge(m), "split-KV merge launch");
+}
+
+int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts, int64_t rows,
+                      int64_t d, void* O, float* LSE, int dtype, void* stream) {
+  g_last_error.clear();
+  if (elem_bytes(dtype) == 0)
+    return fail(FA_ERR_DTYPE, "dtype " + std::to_string(dtype) + " is not FA_F32, FA_F16 or FA_BF16");
+  if (num_parts < 1 || num_parts > kMaxMergeParts)
+    return fail(FA_ERR_SHAPE, "num_parts must be in 1.." + std::to_string(kMaxMergeParts));
+  if (rows < 0) return fail(FA_ERR_SHAPE, "rows must be >= 0");
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_HEAD_DIM, "head dimension d must be 64 or 128 (got " + std::to_string(d) + ")");
+  if (rows == 0) return FA_OK;
+  if (rows * num_parts * (d + 1) >= (int64_t(1) << 40)) return fail(FA_ERR_SHAPE, "too many rows");
+  if (!O_part || !LSE_part || !O || !LSE) return fail(FA_ERR_NULL, "pointers must not be NULL");
+  if (!aligned(O_part, 16) || !aligned(O, 16)) return fail(FA_ERR_ALIGN, "O_part and O must be 16-byte aligned");
+  if (!aligned(LSE_part, 4) || !aligned(LSE, 4)) return fail(FA_ERR_ALIGN, "LSE_part and LSE must be 4-byte aligned");
+  const size_t np = static_cast<size_t>(num_parts), r = static_cast<size_t>(rows);
+  const Region in[2] = {{O_part, np * r * d * sizeof(float), "O_part"},
+                        {LSE_part, np * r * sizeof(float), "LSE_part"}};
+  const Region out[2] = {{O, r * d * elem_bytes(dtype), "O"}, {LSE, r * sizeof(float), "LSE"}};
+  int st = check_aliasing(in, 2, out, 2);
+  if (st != FA_OK) return st;
+  if (iofa::merge_workgroups(rows, d) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::MergeArgs m{O_part, LSE_part, num_parts, rows, d, O, LSE, dtype,
+                    static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_merge(m), "merge launch");
 }
 
 int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, void* S_ws,
@@ -163,6 +257,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 }  // extern "C"

@@ -256,6 +256,31 @@ __device__ inline void interleave_mfma_valu() {
   interleave_step<NMFMA, NDS - LEAD, VPM, 0>();
 }
 
+// Position of a workgroup in the grid.  The logical order (contiguous per
+// XCD, see xcd_logical_id) is ((bh * splits) + split) * qtiles + qt, so the
+// query tiles of one head and key range run side by side on one XCD and
+// share its L2 copy of those keys and values.
+struct GridPos {
+  int bh, split, qt;
+};
+__device__ inline GridPos grid_pos(int num_qtiles, int num_splits, int num_wg) {
+  const int L = xcd_logical_id(blockIdx.x, num_wg);
+  const int rest = L / num_qtiles;
+  return GridPos{rest / num_splits, rest % num_splits, L % num_qtiles};
+}
+
+// Keys of split s out of G: the whole BC-key tiles [s*NT/G, (s+1)*NT/G) of
+// the NT tiles covering N keys (non-empty when G <= NT).  Returns the first
+// key and the key count.
+__device__ inline int2 key_range(int N, int BC, int split, int num_splits) {
+  const int nt = (N + BC - 1) / BC;
+  const int t0 = static_cast<int>(static_cast<int64_t>(split) * nt / num_splits);
+  const int t1 = static_cast<int>(static_cast<int64_t>(split + 1) * nt / num_splits);
+  const int kbeg = t0 * BC;
+  const int kend = t1 * BC < N ? t1 * BC : N;
+  return make_int2(kbeg, kend - kbeg);
+}
+
 // Per wave, tile t of the key sweep (NT tiles) is processed in three steps:
 // its scores in iteration t-1, its softmax in iteration t, its P V product
 // in iteration t+1.  K tile t lives in K stage t%2, copied in iteration t-2;
@@ -266,11 +291,18 @@ __device__ inline void interleave_mfma_valu() {
 //           and scores_{j+1} (K stage 1-P) on the MFMA unit;
 //   bottom  rescale of O if the reference maximum moved; wait for this
 //           iteration's copies; barrier.
-template <class T, int D, int BC>
+//
+// With PARTIAL the workgroup covers only the keys of its split (key_range)
+// and writes the normalised partial output in fp32 to Out[(split*BH + bh),
+// q, :] and its log-sum-exp to Lse[(split*BH + bh), q]; the partials are
+// combined by fa_merge_kernel.  Otherwise (one split) it writes O in the
+// input type and the final LSE.
+template <class T, int D, int BC, bool PARTIAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int N, int num_qtiles, int num_wg, float scale) {
+    const uint16_t* __restrict__ V, void* __restrict__ Out,
+    float* __restrict__ Lse, int N, int BH, int num_qtiles, int num_splits, int num_wg,
+    float scale) {
   using C = FusedCfg<D, BC>;
   using vec8 = typename T::vec8;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::SMEM];
@@ -282,23 +314,25 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
-  const int L = xcd_logical_id(blockIdx.x, num_wg);
-  const int bh = L / num_qtiles, qt = L % num_qtiles;
+  const GridPos gp = grid_pos(num_qtiles, num_splits, num_wg);
+  const int bh = gp.bh, qt = gp.qt;
+  const int2 kr = key_range(N, BC, gp.split, num_splits);
+  const int NK = kr.y;                 // keys of this workgroup
   const size_t head = static_cast<size_t>(bh) * N * D;
   const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const uint16_t* Kh = K + head + static_cast<size_t>(kr.x) * D;
+  const uint16_t* Vh = V + head + static_cast<size_t>(kr.x) * D;
 
-  const int NT = (N + BC - 1) / BC;   // key tiles
-  const bool ragged = (N % BC) != 0;
+  const int NT = (NK + BC - 1) / BC;   // key tiles
+  const bool ragged = (NK % BC) != 0;
   TileCopy<D, BC, false> kcp;
   TileCopy<D, BC, true> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
   // a2 prologue: K_0 and K_1 in flight while Q is loaded
-  kcp.copy(Kh, 0, N, kst[0]);
-  kcp.copy(Kh, BC, N, kst[1]);
+  kcp.copy(Kh, 0, NK, kst[0]);
+  kcp.copy(Kh, BC, NK, kst[1]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
@@ -338,8 +372,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
                        vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
     constexpr int P = decltype(par)::value;
-    kcp.copy(Kh, (j + 2) * BC, N, kst[P]);
-    vcp.copy(Vh, j * BC, N, vst[P]);
+    kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
+    vcp.copy(Vh, j * BC, NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv<1 - P>(p_prev);
     ws.template scores<1 - P>(s_nxt);
@@ -350,8 +384,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
                   vec8 (&p_cur)[C::KSTEPS]) {
     constexpr int P = decltype(par)::value;
-    vcp.copy(Vh, j * BC, N, vst[P]);
-    const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, N - j * BC)
+    vcp.copy(Vh, j * BC, NK, vst[P]);
+    const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
                                : ws.template softmax<false>(s_cur, p_cur, c2, BC);
     if (j > 0) ws.template pv<1 - P>(p_prev);
     bottom(alpha);
@@ -364,8 +398,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     last(P0{}, 0, sa, pb, pa);
   } else {
     // iteration 0: softmax_0 with scores_1
-    kcp.copy(Kh, 2 * BC, N, kst[0]);
-    vcp.copy(Vh, 0, N, vst[0]);
+    kcp.copy(Kh, 2 * BC, NK, kst[0]);
+    vcp.copy(Vh, 0, NK, vst[0]);
     {
       const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
       ws.template scores<1>(sb);
@@ -387,23 +421,37 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     }
   }
 
-  // a7: O = acc / l rounded to the input type; LSE = ln2 * (m + log2 l)
+  // a7: O = acc / l rounded to the input type (or kept fp32 for a partial);
+  // LSE = ln2 * (m + log2 l).  Lane half hi holds columns 32*cb + 8*g + 4*hi
+  // + 0..3 in registers 4*g .. 4*g+3.
   if (q < N) {
     const float inv_l = 1.0f / ws.l_run;
-    uint16_t* Oq = O + head + static_cast<size_t>(q) * D;
+    const float lse = (ws.m_run + __builtin_amdgcn_logf(ws.l_run)) * kLn2;
+    if constexpr (PARTIAL) {
+      const size_t row = (static_cast<size_t>(gp.split) * BH + bh) * N + q;
+      float* Oq = static_cast<float*>(Out) + row * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
+      for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = T::pack(ws.o[cb][4 * g + 0] * inv_l, ws.o[cb][4 * g + 1] * inv_l);
-        w[1] = T::pack(ws.o[cb][4 * g + 2] * inv_l, ws.o[cb][4 * g + 3] * inv_l);
-        *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * ws.hi) = w;
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(Oq + 32 * cb + 8 * g + 4 * ws.hi) =
+              make_float4(ws.o[cb][4 * g + 0] * inv_l, ws.o[cb][4 * g + 1] * inv_l,
+                          ws.o[cb][4 * g + 2] * inv_l, ws.o[cb][4 * g + 3] * inv_l);
+      if (ws.hi == 0) Lse[row] = lse;
+    } else {
+      uint16_t* Oq = static_cast<uint16_t*>(Out) + head + static_cast<size_t>(q) * D;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = T::pack(ws.o[cb][4 * g + 0] * inv_l, ws.o[cb][4 * g + 1] * inv_l);
+          w[1] = T::pack(ws.o[cb][4 * g + 2] * inv_l, ws.o[cb][4 * g + 3] * inv_l);
+          *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * ws.hi) = w;
+        }
       }
+      if (ws.hi == 0) Lse[static_cast<size_t>(bh) * N + q] = lse;
     }
-    if (ws.hi == 0)
-      LSE[static_cast<size_t>(bh) * N + q] =
-          (ws.m_run + __builtin_amdgcn_logf(ws.l_run)) * kLn2;
   }
 }
 
@@ -415,18 +463,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
 // output accumulator; a score is the 8-lane sum of partial dot products.
 // K and V tiles of 32 keys are staged in LDS.
 
-template <int D>
+// With PARTIAL: keys of the workgroup's split only, output rows
+// (split*BH + bh, q) of the fp32 partials (see fa_fwd_16_kernel).
+template <int D, bool PARTIAL>
 __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-    int N, int num_qtiles, int num_wg, float scale) {
+    int N, int BH, int num_qtiles, int num_splits, int num_wg, float scale) {
   constexpr int QPB = 32, TPQ = 8, DPT = D / TPQ, BC = 32, LS = D + 4;
   __shared__ __attribute__((aligned(16))) float Ks[BC * LS];
   __shared__ __attribute__((aligned(16))) float Vs[BC * LS];
 
   const int tid = threadIdx.x;
-  const int L = xcd_logical_id(blockIdx.x, num_wg);
-  const int bh = L / num_qtiles, qt = L % num_qtiles;
+  const GridPos gp = grid_pos(num_qtiles, num_splits, num_wg);
+  const int bh = gp.bh, qt = gp.qt;
+  const int2 kr = key_range(N, BC, gp.split, num_splits);
+  const int kbeg = kr.x, kend = kr.x + kr.y;
   const size_t head = static_cast<size_t>(bh) * N * D;
   const int qi = tid / TPQ, part = tid % TPQ;
   const int q = qt * QPB + qi;
@@ -440,11 +492,11 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
   }
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  for (int k0 = 0; k0 < N; k0 += BC) {
+  for (int k0 = kbeg; k0 < kend; k0 += BC) {
     for (int i = tid; i < BC * D / 4; i += 256) {
       const int row = i / (D / 4), c4 = i % (D / 4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (k0 + row < N) {
+      if (k0 + row < kend) {
         kv = *reinterpret_cast<const float4*>(K + head + static_cast<size_t>(k0 + row) * D + 4 * c4);
         vv = *reinterpret_cast<const float4*>(V + head + static_cast<size_t>(k0 + row) * D + 4 * c4);
       }
@@ -463,7 +515,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
       part_dot += __shfl_xor(part_dot, 1, TPQ);
       part_dot += __shfl_xor(part_dot, 2, TPQ);
       part_dot += __shfl_xor(part_dot, 4, TPQ);
-      sc[j] = (k0 + j < N) ? part_dot * scale : -__builtin_inff();
+      sc[j] = (k0 + j < kend) ? part_dot * scale : -__builtin_inff();
       mx = fmaxf(mx, sc[j]);
     }
     const float m_new = fmaxf(m_run, mx);
@@ -488,9 +540,11 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
   }
 
   if (q < N) {
+    const size_t row = PARTIAL ? (static_cast<size_t>(gp.split) * BH + bh) * N + q
+                               : static_cast<size_t>(bh) * N + q;
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) O[head + static_cast<size_t>(q) * D + c0 + e] = ov[e] / l_run;
-    if (part == 0) LSE[static_cast<size_t>(bh) * N + q] = m_run + logf(l_run);
+    for (int e = 0; e < DPT; ++e) O[row * D + c0 + e] = ov[e] / l_run;
+    if (part == 0) LSE[row] = m_run + logf(l_run);
   }
 }
 
@@ -501,38 +555,61 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
 template <int D>
 constexpr int kFusedBC = D == 128 ? 32 : 64;
 
-template <class T, int D, int BC = kFusedBC<D>>
-static hipError_t launch16(const FwdArgs& a) {
+int fused_key_tile(int dtype, int64_t d) {
+  if (dtype == kDtypeF32) return 32;
+  return d == 128 ? kFusedBC<128> : kFusedBC<64>;
+}
+
+int64_t fused_query_tile(int dtype) {
+  return dtype == kDtypeF32 ? 32 : FusedCfg<128, kFusedBC<128>>::BR;
+}
+
+template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
+static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) {
   using C = FusedCfg<D, BC>;
   const int qtiles = static_cast<int>((a.N + C::BR - 1) / C::BR);
-  const int64_t wg = a.BH * qtiles;
-  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
-                     a.stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
-                     static_cast<const uint16_t*>(a.V), static_cast<uint16_t*>(a.O), a.LSE,
-                     static_cast<int>(a.N), qtiles, static_cast<int>(wg), a.scale);
+  const int64_t wg = a.BH * splits * qtiles;
+  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC, PARTIAL>), dim3(static_cast<unsigned>(wg)),
+                     dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.Q),
+                     static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), out, lse,
+                     static_cast<int>(a.N), static_cast<int>(a.BH), qtiles, splits,
+                     static_cast<int>(wg), a.scale);
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch32(const FwdArgs& a) {
+template <int D, bool PARTIAL>
+static hipError_t launch32(const FwdArgs& a, int splits, float* out, float* lse) {
   const int qtiles = static_cast<int>((a.N + 31) / 32);
-  const int64_t wg = a.BH * qtiles;
-  hipLaunchKernelGGL((fa_fwd_f32_kernel<D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+  const int64_t wg = a.BH * splits * qtiles;
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, PARTIAL>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
                      a.stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
-                     static_cast<const float*>(a.V), static_cast<float*>(a.O), a.LSE,
-                     static_cast<int>(a.N), qtiles, static_cast<int>(wg), a.scale);
+                     static_cast<const float*>(a.V), out, lse, static_cast<int>(a.N),
+                     static_cast<int>(a.BH), qtiles, splits, static_cast<int>(wg), a.scale);
   return hipGetLastError();
 }
 
-int64_t fused_workgroups(int dtype, int64_t BH, int64_t N) {
-  const int64_t br = (dtype == kDtypeF32) ? 32 : FusedCfg<128, kFusedBC<128>>::BR;
-  return BH * ((N + br - 1) / br);
+template <bool PARTIAL>
+static hipError_t launch_any(const FwdArgs& a, int splits, void* out, float* lse) {
+  if (a.dtype == kDtypeBF16)
+    return a.d == 128 ? launch16<Bf16, 128, PARTIAL>(a, splits, out, lse)
+                      : launch16<Bf16, 64, PARTIAL>(a, splits, out, lse);
+  if (a.dtype == kDtypeF16)
+    return a.d == 128 ? launch16<F16, 128, PARTIAL>(a, splits, out, lse)
+                      : launch16<F16, 64, PARTIAL>(a, splits, out, lse);
+  float* o = static_cast<float*>(out);
+  return a.d == 128 ? launch32<128, PARTIAL>(a, splits, o, lse)
+                    : launch32<64, PARTIAL>(a, splits, o, lse);
 }
 
-hipError_t launch_fused(const FwdArgs& a) {
-  if (a.dtype == kDtypeBF16) return a.d == 128 ? launch16<Bf16, 128>(a) : launch16<Bf16, 64>(a);
-  if (a.dtype == kDtypeF16) return a.d == 128 ? launch16<F16, 128>(a) : launch16<F16, 64>(a);
-  return a.d == 128 ? launch32<128>(a) : launch32<64>(a);
+int64_t fused_workgroups(int dtype, int64_t BH, int64_t N, int64_t splits) {
+  const int64_t br = fused_query_tile(dtype);
+  return BH * splits * ((N + br - 1) / br);
+}
+
+hipError_t launch_fused(const FwdArgs& a) { return launch_any<false>(a, 1, a.O, a.LSE); }
+
+hipError_t launch_fused_partial(const FwdArgs& a, int splits, float* O_part, float* LSE_part) {
+  return launch_any<true>(a, splits, O_part, LSE_part);
 }
 
 }  // namespace iofa

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace iofa {
 
 constexpr int kDtypeF32 = 0;
@@ -32,12 +34,34 @@ struct NaiveArgs {
   int64_t ldS;  // row stride of S and P in elements (N rounded up to 8)
 };
 
+// Merge of G fp32 partials (G, rows, d) / (G, rows) into O (rows, d) in
+// `dtype` and LSE (rows).
+struct MergeArgs {
+  const float* O_part;
+  const float* LSE_part;
+  int G;
+  int64_t rows;
+  int64_t d;
+  void* O;
+  float* LSE;
+  int dtype;
+  hipStream_t stream;
+};
+
+// Keys per tile and query rows per workgroup of the fused kernels.
+int fused_key_tile(int dtype, int64_t d);
+int64_t fused_query_tile(int dtype);
 // Workgroups the fused launch uses (for the grid-size limit check).
-int64_t fused_workgroups(int dtype, int64_t BH, int64_t N);
+int64_t fused_workgroups(int dtype, int64_t BH, int64_t N, int64_t splits);
+int64_t merge_workgroups(int64_t rows, int64_t d);
 // Largest grid among the naive path's three launches.
 int64_t naive_max_workgroups(int dtype, int64_t BH, int64_t N);
 
 hipError_t launch_fused(const FwdArgs& a);
+// Partial pass of the split-KV forward: fp32 O_part (splits, B*H, N, d) and
+// LSE_part (splits, B*H, N).
+hipError_t launch_fused_partial(const FwdArgs& a, int splits, float* O_part, float* LSE_part);
+hipError_t launch_merge(const MergeArgs& a);
 hipError_t launch_naive(const NaiveArgs& a);
 
 constexpr int64_t kNaiveMaxN = 32768;

@@ -1,0 +1,97 @@
+// Merge of partial attention results over disjoint key ranges (gfx950).
+//
+// The special-jiahao.github.io "Flash Attention" note, section
+// "增量求解 softmax", combines the local softmaxes of two blocks of a vector
+// into the global one: the global maximum, each block's denominator rescaled
+// by e^{m(block) - m(x)}, and each block's local result weighted by its
+// rescaled denominator over the global one.  For G blocks of keys with
+// partial outputs O_g (each normalised by its own denominator) and
+// log-sum-exps LSE_g = m_g + ln l_g this reads, per query row,
+//     LSE = ln sum_g e^{LSE_g},      O = sum_g e^{LSE_g - LSE} O_g,
+// since e^{LSE_g - LSE} = l(block g)^global / l(x).
+//
+// Memory-bound: each row reads G*(d + 1) fp32 values and writes d outputs
+// and one LSE.  A row is handled by d/4 threads, each owning 4 consecutive
+// columns (16-byte loads); a 256-thread workgroup covers 256/(d/4) rows.
+// The largest LSE_g is the reference, so no exponential exceeds 1; exp and
+// log are the accurate library functions (the kernel is bandwidth-bound).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace iofa {
+
+namespace {
+
+template <int KIND>   // 0: fp32 output, 1: fp16, 2: bf16
+__device__ inline void store4(void* O, size_t off, float4 v) {
+  if constexpr (KIND == 0) {
+    *reinterpret_cast<float4*>(static_cast<float*>(O) + off) = v;
+  } else {
+    using T = typename std::conditional<KIND == 2, Bf16, F16>::type;
+    u32x2 w;
+    w[0] = T::pack(v.x, v.y);
+    w[1] = T::pack(v.z, v.w);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(O) + off) = w;
+  }
+}
+
+template <int KIND, int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ Op,
+                                                       const float* __restrict__ Lp, int G,
+                                                       int64_t rows, void* __restrict__ O,
+                                                       float* __restrict__ LSE) {
+  constexpr int TPR = D / 4;           // threads per row
+  constexpr int RPB = 256 / TPR;       // rows per workgroup
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+
+  float ref = -__builtin_inff();
+  for (int g = 0; g < G; ++g) ref = fmaxf(ref, Lp[g * rows + row]);
+  const float base = (ref == -__builtin_inff()) ? 0.f : ref;
+  float total = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g = 0; g < G; ++g) {
+    const float w = expf(Lp[g * rows + row] - base);
+    const float4 o = *reinterpret_cast<const float4*>(Op + (g * rows + row) * D + 4 * c4);
+    total += w;
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
+  }
+  // total >= 1 whenever some block has keys (the reference block weighs 1)
+  const float inv = total > 0.f ? 1.f / total : 0.f;
+  store4<KIND>(O, static_cast<size_t>(row) * D + 4 * c4,
+               make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+  if (c4 == 0) LSE[row] = total > 0.f ? base + logf(total) : -__builtin_inff();
+}
+
+template <int KIND, int D>
+hipError_t launch_merge_t(const MergeArgs& a) {
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t wg = (a.rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((fa_merge_kernel<KIND, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+                     a.stream, a.O_part, a.LSE_part, a.G, a.rows, a.O, a.LSE);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t merge_workgroups(int64_t rows, int64_t d) {
+  const int64_t rpb = 256 / (d / 4);
+  return (rows + rpb - 1) / rpb;
+}
+
+hipError_t launch_merge(const MergeArgs& a) {
+  if (a.d == 128) {
+    if (a.dtype == kDtypeBF16) return launch_merge_t<2, 128>(a);
+    if (a.dtype == kDtypeF16) return launch_merge_t<1, 128>(a);
+    return launch_merge_t<0, 128>(a);
+  }
+  if (a.dtype == kDtypeBF16) return launch_merge_t<2, 64>(a);
+  if (a.dtype == kDtypeF16) return launch_merge_t<1, 64>(a);
+  return launch_merge_t<0, 64>(a);
+}
+
+}  // namespace iofa

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_fwd", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
+        "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
+        "fa_merge_partials", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
         "fa_last_error", "fa_version"])
 
 
@@ -47,7 +48,7 @@ def test_symbols_have_c_linkage():
 
 
 def test_status_strings_and_version(lib):
-    assert iofa.fa_version() == 100
+    assert iofa.fa_version() == 200
     assert iofa.fa_status_string(0) == "ok"
     for s in range(1, 9):
         assert iofa.fa_status_string(s) not in ("ok", "unknown status")
@@ -134,3 +135,69 @@ def test_python_binding_raises_without_compute():
     q = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         iofa.fa_fwd(q, q, q[..., :32], q.clone(), None, 0.1)
+
+
+# ------------------------------------------------- split-KV and merge (no GPU)
+
+WS = A * 9
+
+
+def splitkv(lib, ws=WS, ws_bytes=1 << 30, splits=4, lse=L, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, B=2, H=2, N=4096, d=128, scale=0.1, dtype=2)
+    args.update(kw)
+    lse_p = ctypes.cast(ctypes.c_void_p(lse), ctypes.POINTER(ctypes.c_float)) if lse else None
+    return lib.fa_fwd_splitkv(*(ctypes.c_void_p(args[x]) for x in "qkvo"), lse_p,
+                              ctypes.c_void_p(ws), ws_bytes, splits, args["B"], args["H"],
+                              args["N"], args["d"], args["scale"], args["dtype"], None)
+
+
+def test_split_count_policy(lib):
+    # one GPU's 8-way head share of the N=4096 d=128 workload: 128 workgroups
+    # per split, so 4 splits reach 512
+    assert iofa.fa_splitkv_num_splits(2, 2, 4096, 128, 2, 0) == 4
+    assert iofa.fa_splitkv_num_splits(2, 16, 4096, 128, 2, 0) == 1     # already 1024 WGs
+    assert iofa.fa_splitkv_num_splits(1, 1, 100, 128, 2, 99) == 4      # 4 key tiles of 32
+    assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 2, 99) == 2       # 2 key tiles of 64
+    assert iofa.fa_splitkv_num_splits(1, 1, 1 << 20, 128, 2, 1000) == 64
+    assert iofa.fa_splitkv_num_splits(1, 1, 100, 96, 2, 0) == 0        # invalid d
+    assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 5, 0) == 0        # invalid dtype
+
+
+def test_split_workspace_bytes(lib):
+    assert iofa.fa_splitkv_workspace_bytes(2, 2, 4096, 128, 2, 4) == 4 * 4 * 4096 * 129 * 4
+    assert iofa.fa_splitkv_workspace_bytes(2, 16, 4096, 128, 2, 0) == 0      # G = 1
+    assert iofa.fa_splitkv_workspace_bytes(2, 2, 4096, 128, 2, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), 1), (dict(ws_bytes=100), 2), (dict(ws=WS + 8), 5), (dict(ws=Q), 7),
+    (dict(ws=O + 64), 7), (dict(dtype=9), 4), (dict(d=80), 3), (dict(lse=0), 1),
+    (dict(scale=float("inf")), 6), (dict(o=K), 7),
+])
+def test_splitkv_rejects_bad_arguments(lib, kw, status):
+    st = splitkv(lib, **kw)
+    assert st == status, (kw, st, iofa.fa_last_error())
+    assert iofa.fa_last_error() != ""
+
+
+def test_splitkv_empty_problem(lib):
+    assert splitkv(lib, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, N=0) == 0
+
+
+def merge(lib, op=Q, lp=K, g=3, rows=10, d=64, o=O, lse=L, dtype=2):
+    f = lambda x: ctypes.cast(ctypes.c_void_p(x), ctypes.POINTER(ctypes.c_float)) if x else None
+    return lib.fa_merge_partials(f(op), f(lp), g, rows, d, ctypes.c_void_p(o), f(lse), dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(g=0), 2), (dict(g=5000), 2), (dict(rows=-1), 2), (dict(d=32), 3), (dict(dtype=4), 4),
+    (dict(op=0), 1), (dict(lse=0), 1), (dict(op=Q + 4), 5), (dict(lse=L + 1), 5),
+    (dict(o=Q), 7), (dict(lse=K + 8), 7),
+])
+def test_merge_rejects_bad_arguments(lib, kw, status):
+    st = merge(lib, **kw)
+    assert st == status, (kw, st, iofa.fa_last_error())
+
+
+def test_merge_of_no_rows_is_a_no_op(lib):
+    assert merge(lib, op=0, lp=0, o=0, lse=0, rows=0) == 0

@@ -1,0 +1,125 @@
+"""GPU parity of the split-KV forward and of the merge entry point against
+the fp64 oracle (partial attention over key ranges, and the block merge),
+called through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_softmax_04_amd as iofa
+import oracle
+from helpers import TOL, assert_parity, errors, oracle_full, oracle_rows, sample_rows, widen
+from workloads import default_scale, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    iofa.load_library()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _key_tile(dtype, d):
+    return 32 if (dtype == "fp32" or d == 128) else 64
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv_matches_oracle(dtype, d, dev):
+    for N, splits in ((65, 2), (200, 3), (1000, 0), (1025, 5), (777, 64), (300, 1)):
+        q, k, v = make_qkv(1, 2, N, d, dtype, seed_base=31 * N + d)
+        scale = default_scale(d)
+        g = iofa.fa_splitkv_num_splits(1, 2, N, d, q.dtype, splits)
+        _say(f"splitkv {dtype} d={d} N={N} requested={splits} G={g}")
+        o, lse = iofa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), scale, splits)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+        assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype,
+                      f"splitkv {dtype} d={d} N={N} G={g}")
+
+
+def test_splitkv_one_gpu_share_of_the_headline_workload(dev):
+    # B=2 H=2 N=4096 d=128: the per-GPU share of the B=2 H=16 workload split
+    # by heads over 8 GPUs; 128 query-tile workgroups, so 4 key ranges
+    q, k, v = make_qkv(2, 2, 4096, 128, "bf16", seed_base=3000)
+    scale = default_scale(128)
+    assert iofa.fa_splitkv_num_splits(2, 2, 4096, 128, q.dtype, 0) == 4
+    o, lse = iofa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, seed=3)
+    o_ref, lse_ref = oracle_rows(q, k, v, scale, rows)
+    res = assert_parity(o.cpu()[:, :, rows], lse.cpu()[:, :, rows], o_ref, lse_ref, q.dtype,
+                        "splitkv B2 H2 N4096")
+    _say(f"  max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
+
+
+def test_splitkv_stress_distribution(dev):
+    q, k, v = make_qkv(1, 2, 2000, 128, "fp16", seed_base=5555, dist="stress")
+    scale = default_scale(128)
+    o, lse = iofa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), scale, 5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, "splitkv stress G=5")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64), ("fp32", 128)])
+def test_splitkv_partials_match_partial_attention(dtype, d, dev):
+    # the partial pass on its own: the workspace holds, per key range, the
+    # attention over that range's keys (oracle.partial_attention)
+    B, H, N, G = 1, 2, 700, 3
+    q, k, v = make_qkv(B, H, N, d, dtype, seed_base=77 + d)
+    scale = default_scale(d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    nbytes = iofa.fa_splitkv_workspace_bytes(B, H, N, d, q.dtype, G)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    iofa.fa_fwd_splitkv(qd, kd, vd, o, lse, ws, scale, G)
+    torch.cuda.synchronize()
+    flat = ws.view(torch.float32).cpu()
+    o_part = flat[:G * B * H * N * d].view(G, B, H, N, d).double().numpy()
+    lse_part = flat[G * B * H * N * d:].view(G, B, H, N).double().numpy()
+    bc = _key_tile(dtype, d)
+    nt = (N + bc - 1) // bc
+    tol = TOL[q.dtype]
+    for s in range(G):
+        k0, k1 = s * nt // G * bc, min(N, (s + 1) * nt // G * bc)
+        po, pl = oracle.partial_attention(widen(q), widen(k), widen(v),
+                                          float(np.float32(scale)), k0, k1)
+        d_o = np.abs(o_part[s] - po)
+        assert d_o.max() <= tol["o_abs"], (s, d_o.max())
+        assert np.linalg.norm(o_part[s] - po) / np.linalg.norm(po) <= tol["o_relf"]
+        assert np.abs(lse_part[s] - pl).max() <= tol["lse_abs"], s
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"splitkv {dtype} d={d} G=3")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_entry_point(out_dtype, d, dev):
+    rng = np.random.default_rng(d)
+    for G, rows in ((1, 5), (2, 333), (7, 1000)):
+        o_part = rng.standard_normal((G, rows, d)).astype(np.float32)
+        lse_part = rng.uniform(-20, 20, (G, rows)).astype(np.float32)
+        if G > 1:
+            lse_part[0, ::3] = -np.inf            # blocks without keys
+        o_ref, lse_ref = oracle.merge_partials(o_part.astype(np.float64),
+                                               lse_part.astype(np.float64))
+        o = torch.empty(rows, d, dtype=out_dtype, device=dev)
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+        iofa.fa_merge_partials(torch.from_numpy(o_part).to(dev),
+                               torch.from_numpy(lse_part).to(dev), o, lse)
+        torch.cuda.synchronize()
+        got = widen(o.cpu())
+        u = {torch.float32: 2.0 ** -24, torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+        # output rounding u|O| plus fp32 arithmetic over G terms
+        bound = u[out_dtype] * np.abs(o_ref) + 1e-5 * (1 + np.abs(o_ref))
+        assert np.all(np.abs(got - o_ref) <= bound), (G, rows, np.abs(got - o_ref).max())
+        assert np.abs(lse.cpu().double().numpy() - lse_ref).max() <= 1e-5 * (1 + np.abs(lse_ref).max())
