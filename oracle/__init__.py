@@ -32,8 +32,10 @@ from .attention import (
 )
 from .softmax import (
     local_softmax,
-    two_block_softmax,
+    online_row_stats,
     online_softmax_output,
+    softmax_rows,
+    two_block_softmax,
 )
 from .tiled import tiled_online_attention
 from .mac_count import standard_attention_mac
@@ -48,6 +50,8 @@ __all__ = [
     "local_softmax",
     "two_block_softmax",
     "online_softmax_output",
+    "softmax_rows",
+    "online_row_stats",
     "tiled_online_attention",
     "standard_attention_mac",
     "partial_attention",

@@ -92,3 +92,33 @@ def online_softmax_output(s, v, block=1):
         z = alpha * z + e @ vb                   # z_{t+1}
         m = m_new
     return z / l, m, l
+
+
+def softmax_rows(x):
+    """Row-wise softmax of a 2-D array by the per-block quantities of
+    [jiahao] "增量求解 softmax" taken over the whole row (one block):
+    returns (y, lse) with y[r] = s(row r) and lse[r] = m + ln l."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    lse = np.empty(x.shape[0])
+    for r in range(x.shape[0]):
+        m, _, l, s = local_softmax(x[r])
+        y[r] = s
+        lse[r] = m + np.log(l) if l > 0 else -np.inf
+    return y, lse
+
+
+def online_row_stats(x, block):
+    """Running maximum and denominator of one row, adding ``block`` scores at
+    a time ([xinc] "7. Online Softmax": a new block rescales the old l by
+    e^{m_old - m_new} and adds its own terms).  Returns (m, l)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, l = -np.inf, 0.0
+    for t0 in range(0, x.shape[0], block):
+        xb = x[t0:t0 + block]
+        m_new = max(m, xb.max())
+        if m_new == -np.inf:
+            continue
+        l = _rescale(m, m_new) * l + np.exp(xb - m_new).sum()
+        m = m_new
+    return m, l

@@ -500,3 +500,37 @@ def test_planted_merge_mistakes_fail_a_pin(kind):
     o, lse = bad_merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
     o_ref, lse_ref = oracle.standard_attention(q, k, v, 0.7)
     assert np.abs(o - o_ref).max() > 1e-6 or np.abs(lse - lse_ref).max() > 1e-6
+
+
+# ------------------------------------------------------- standalone softmax
+
+def test_softmax_rows_against_scipy_and_brute_force():
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((7, 50)) * 5
+    x[2, :] = 3.0                                   # constant row: uniform weights
+    x[3, 7] = 80.0                                  # one dominant entry
+    y, lse = oracle.softmax_rows(x)
+    assert np.abs(y - softmax(x, axis=1)).max() <= 1e-15
+    assert np.abs(lse - logsumexp(x, axis=1)).max() <= 1e-13
+    assert np.abs(y[2] - 1 / 50).max() <= 1e-16
+    assert abs(y[3, 7] - 1.0) <= 1e-15
+    assert np.abs(y.sum(axis=1) - 1).max() <= 1e-14
+    # 40-digit brute force on one row, no max subtraction
+    with decimal.localcontext() as ctx:
+        ctx.prec = 40
+        row = [D(repr(float(t))) for t in x[0]]
+        den = sum(v.exp() for v in row)
+        for j, v in enumerate(row):
+            assert abs(float(v.exp() / den) - y[0, j]) <= 1e-15 * max(1.0, y[0, j])
+        assert abs(float(den.ln()) - lse[0]) <= 1e-13
+
+
+@pytest.mark.parametrize("n,block", [(1, 1), (17, 1), (17, 4), (1000, 33), (1000, 1000)])
+def test_online_row_stats_match_two_pass(n, block):
+    rng = np.random.default_rng(n + block)
+    x = rng.standard_normal(n) * 10 + np.linspace(0, 30, n)    # maximum moves late
+    m, l = oracle.online_row_stats(x, block)
+    m2, _, l2, _ = oracle.local_softmax(x)
+    assert m == m2
+    assert abs(l - l2) <= 1e-13 * l2
