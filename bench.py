@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--no-naive", action="store_true", help="skip the naive contrast")
     p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
+    p.add_argument("--no-softmax", action="store_true", help="skip the row-softmax measurement")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -450,6 +451,38 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     }
 
 
+def softmax_measure(args, torch, iofa, dev):
+    """The standalone row softmax on bf16 rows that fit one workgroup (x read
+    once, y written once) and on long rows (x read twice).  Roofline: HBM;
+    algorithmic bytes = read x once + write y once + 4 bytes of LSE per
+    row."""
+    out = []
+    for rows, n in ((32768, 8192), (64, 1 << 22)):
+        g = torch.Generator(device=dev).manual_seed(rows)
+        x = (torch.randn((rows, n), generator=g, device=dev) * 4).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+        nb = iofa.fa_softmax_workspace_bytes(rows, n, x.dtype)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        steps = max(5, min(args.steps, 30))
+        _, ms = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
+                              steps, 3, torch)
+        alg = rows * n * 2 * 2 + rows * 4
+        reads = 1 if nb == 0 else 2
+        moved = rows * n * 2 * (reads + 1) + rows * 4
+        gbs = alg / (ms * 1e-3) / 1e9
+        out.append({
+            "workload": f"bf16 rows={rows} n={n}", "ms": round(ms, 4),
+            "x_reads": reads,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": alg},
+            "moved_bytes_per_s_GBs": round(moved / (ms * 1e-3) / 1e9, 1),
+        })
+        del x, y, ws
+    return out
+
+
 def main():
     args = parse()
     if args.sq_from:
@@ -563,6 +596,10 @@ def main():
     if not args.no_splitkv and spec["dtype"] != "fp32":
         line["splitkv_contrast"] = splitkv_contrast(spec, args, torch, iofa, dev)
         print(f"[bench] split-KV: {line['splitkv_contrast']}", file=sys.stderr, flush=True)
+
+    if not args.no_softmax:
+        line["softmax_rows"] = softmax_measure(args, torch, iofa, dev)
+        print(f"[bench] row softmax: {line['softmax_rows']}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)

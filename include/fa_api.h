@@ -171,6 +171,35 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, in
 int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts, int64_t rows,
                       int64_t d, void* O, float* LSE, int dtype, void* stream);
 
+/*
+ * Row softmax Y[r, :] = e^{X[r, :] - m_r} / l_r with m_r the row maximum and
+ * l_r = sum_j e^{X[r, j] - m_r}; LSE[r] = m_r + ln l_r.  The online softmax
+ * of xinc.fun archive 235, section "7. Online Softmax" (a running maximum and
+ * denominator, the old denominator rescaled by e^{m_old - m_new} when a
+ * block raises the maximum), as a memory-bound operation of its own:
+ *   rows of at most 8192 (16-bit) / 4096 (fp32) elements are read once and
+ *   written once; longer rows are cut into chunks of that size whose
+ *   (m, l) pairs are combined with the block merge of the
+ *   special-jiahao.github.io "Flash Attention" note ("增量求解 softmax"),
+ *   reading X twice (the three-pass maximum / sum / normalise form reads it
+ *   three times).
+ *   X    in:  (rows, n) contiguous, `dtype`, element-aligned (rows of a
+ *             length that keeps them 16-byte aligned use 16-byte accesses).
+ *   Y    out: (rows, n) contiguous, `dtype` (RNE); may equal X (in place),
+ *             must not otherwise overlap it.
+ *   LSE  out: (rows) fp32, or NULL.
+ *   workspace  caller-owned device memory of fa_softmax_workspace_bytes()
+ *             bytes, 8-byte aligned; NULL allowed when that size is 0.
+ * Arithmetic is fp32 for every dtype.  rows or n equal to 0: nothing is
+ * enqueued.  Errors as fa_fwd.
+ */
+int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_softmax_rows needs: rows * chunks * 8 for rows longer
+ * than one chunk, else 0 (also for invalid arguments). */
+size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype);
+
 /* Bytes of ONE naive workspace (S or P): B * H * N * ldS * sizeof(dtype),
  * ldS = N rounded up to a multiple of 8.  Returns 0 for an invalid dtype
  * or negative sizes. */

@@ -1,7 +1,8 @@
 """Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
 
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_splitkv_num_splits``,
-``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_naive_fwd``,
+``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
+``fa_softmax_workspace_bytes``, ``fa_naive_fwd``,
 ``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
 ``fa_version`` carry the names
 and meaning of the entry points declared in ``include/fa_api.h``; they only
@@ -24,7 +25,8 @@ import torch
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
-    "fa_merge_partials", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
+    "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "softmax",
+    "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
     "fa_last_error", "fa_version", "forward", "forward_splitkv", "naive_forward",
     "default_scale",
 ]
@@ -72,6 +74,10 @@ def load_library():
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_merge_partials.argtypes = [fp, fp, ctypes.c_int, i64, i64, vp, fp, ctypes.c_int, vp]
     lib.fa_merge_partials.restype = ctypes.c_int
+    lib.fa_softmax_rows.argtypes = [vp, vp, fp, i64, i64, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_softmax_rows.restype = ctypes.c_int
+    lib.fa_softmax_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+    lib.fa_softmax_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_naive_fwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, i64, i64, i64, i64,
                                  ctypes.c_float, ctypes.c_int, vp]
     lib.fa_naive_fwd.restype = ctypes.c_int
@@ -185,6 +191,42 @@ def fa_merge_partials(o_part, lse_part, o, lse, stream=None):
         st = lib.fa_merge_partials(_fptr(o_part), _fptr(lse_part), G, rows, d, _ptr(o),
                                    _fptr(lse), _DTYPE_CODE[o.dtype], _stream(stream, o.device))
     _check(st)
+
+
+def fa_softmax_rows(x, y, lse=None, workspace=None, stream=None):
+    """Row softmax of the 2-D tensor x into y (same shape and dtype; may be
+    x itself); lse (rows,) fp32 or None; workspace a byte tensor of at least
+    fa_softmax_workspace_bytes() bytes or None when that is 0."""
+    lib = load_library()
+    if x.dim() != 2 or y.shape != x.shape or y.dtype != x.dtype or not x.is_contiguous() \
+            or not y.is_contiguous():
+        raise ValueError("x and y must be contiguous 2-D tensors of one shape and dtype")
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    rows, n = (int(t) for t in x.shape)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (rows,)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 (rows,) tensor")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(x.device):
+        st = lib.fa_softmax_rows(_ptr(x), _ptr(y), _fptr(lse), rows, n, _DTYPE_CODE[x.dtype],
+                                 _ptr(workspace), ws_bytes, _stream(stream, x.device))
+    _check(st)
+
+
+def fa_softmax_workspace_bytes(rows, n, dtype):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_softmax_workspace_bytes(rows, n, code))
+
+
+def softmax(x, want_lse=False, stream=None):
+    """Allocate y (and lse, workspace) and run fa_softmax_rows on a 2-D x."""
+    y = torch.empty_like(x)
+    lse = torch.empty(x.shape[0], dtype=torch.float32, device=x.device) if want_lse else None
+    nbytes = fa_softmax_workspace_bytes(x.shape[0], x.shape[1], x.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    fa_softmax_rows(x, y, lse, ws, stream)
+    return (y, lse) if want_lse else y
 
 
 def fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream=None):

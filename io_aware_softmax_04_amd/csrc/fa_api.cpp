@@ -233,6 +233,53 @@ int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   return hip_status(iofa::launch_naive(a), "naive forward launch");
 }
 
+size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype) {
+  if (elem_bytes(dtype) == 0 || rows < 0 || n < 0) return 0;
+  const int64_t chunk = iofa::softmax_chunk(dtype);
+  if (n <= chunk) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>((n + chunk - 1) / chunk) * 2 * sizeof(float);
+}
+
+int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  const int e = elem_bytes(dtype);
+  if (e == 0)
+    return fail(FA_ERR_DTYPE, "dtype " + std::to_string(dtype) + " is not FA_F32, FA_F16 or FA_BF16");
+  if (rows < 0 || n < 0) return fail(FA_ERR_SHAPE, "rows and n must be >= 0");
+  if (rows == 0 || n == 0) return FA_OK;
+  const int64_t chunk = iofa::softmax_chunk(dtype);
+  const int64_t chunks = (n + chunk - 1) / chunk;
+  if (rows * chunks >= (int64_t(1) << 31) || chunks >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  if (!X || !Y) return fail(FA_ERR_NULL, "X and Y must not be NULL");
+  if (!aligned(X, e) || !aligned(Y, e)) return fail(FA_ERR_ALIGN, "X and Y must be element-aligned");
+  if (LSE && !aligned(LSE, 4)) return fail(FA_ERR_ALIGN, "LSE must be 4-byte aligned");
+  const size_t need = fa_softmax_workspace_bytes(rows, n, dtype);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_NULL, "workspace must not be NULL for rows longer than " +
+                                                 std::to_string(chunk));
+    if (!aligned(workspace, 8)) return fail(FA_ERR_ALIGN, "workspace must be 8-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_SHAPE, "workspace holds " + std::to_string(workspace_bytes) +
+                                    " bytes, rows of this length need " + std::to_string(need));
+  }
+  // Y == X (in place) is allowed: every workgroup reads its chunk in full
+  // before writing it, and pass 2 starts after pass 1.  Partial overlap is not.
+  const size_t bytes = static_cast<size_t>(rows) * static_cast<size_t>(n) * e;
+  const Region in[1] = {{X, Y == X ? 0 : bytes, "X"}};
+  const Region out[3] = {{Y, bytes, "Y"}, {LSE, LSE ? static_cast<size_t>(rows) * 4 : 0, "LSE"},
+                         {workspace, need, "workspace"}};
+  int st = check_aliasing(in, 1, out, 3);
+  if (st == FA_OK && Y == X) {
+    const Region xin[1] = {{X, bytes, "X"}};
+    st = check_aliasing(xin, 1, out + 1, 2);
+  }
+  if (st != FA_OK) return st;
+  iofa::SoftmaxArgs a{X, Y, LSE, rows, n, dtype, workspace, static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_softmax(a), "softmax launch");
+}
+
 size_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
   const int e = elem_bytes(dtype);
   if (e == 0 || B < 0 || H < 0 || N < 0) return 0;

@@ -48,6 +48,22 @@ struct MergeArgs {
   hipStream_t stream;
 };
 
+// Row softmax of X (rows, n) into Y; workspace: rows * chunks float2 (m, l)
+// pairs for rows longer than one chunk.
+struct SoftmaxArgs {
+  const void* X;
+  void* Y;
+  float* LSE;   // may be NULL
+  int64_t rows;
+  int64_t n;
+  int dtype;
+  void* workspace;
+  hipStream_t stream;
+};
+// Elements of a row one workgroup covers.
+int64_t softmax_chunk(int dtype);
+hipError_t launch_softmax(const SoftmaxArgs& a);
+
 // Keys per tile and query rows per workgroup of the fused kernels.
 int fused_key_tile(int dtype, int64_t d);
 int64_t fused_query_tile(int dtype);

@@ -1,0 +1,101 @@
+"""GPU parity of the standalone row softmax (fa_softmax_rows) against the
+fp64 oracle's row softmax, through the C ABI.
+
+Tolerance: the output is rounded once to its type (u|y|, u = 2^-24 fp32,
+2^-11 fp16, 2^-8 bf16; below the smallest normal fp16 value 2^-14 the
+rounding error is at most half the subnormal spacing, 2^-25, absolute); the
+fp32 arithmetic (exponentials, sums of at most 16 terms per thread, then
+256-way and chunk-way merges) adds a relative error below 4e-6.
+LSE: 4e-6 * (1 + |LSE|)."""
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_softmax_04_amd as iofa
+import oracle
+from helpers import UNIT_ROUNDOFF, widen
+
+pytestmark = pytest.mark.gpu
+
+DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+REL = 4e-6
+# absolute floor of the output rounding (subnormal range of the output type)
+ABS_FLOOR = {torch.float32: 2.0 ** -150, torch.float16: 2.0 ** -25, torch.bfloat16: 2.0 ** -134}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    iofa.load_library()
+    return torch.device("cuda:0")
+
+
+def _inputs(rows, n, dtype, seed, spread=5.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((rows, n), generator=g) * spread
+    if n > 1:
+        x[0, n // 2] += 40.0                       # one dominant entry in row 0
+        x[-1] += torch.linspace(0, 30, n)          # maximum reached late in the last row
+    return x.to(DT[dtype]).contiguous()
+
+
+def _check(x, y, lse, label):
+    y_ref, lse_ref = oracle.softmax_rows(widen(x))
+    got = widen(y.cpu())
+    u = UNIT_ROUNDOFF[x.dtype]
+    excess = np.abs(got - y_ref) - (u + REL) * np.abs(y_ref) - ABS_FLOOR[x.dtype]
+    assert excess.max() <= 0, f"{label}: worst excess {excess.max():.3e}"
+    if lse is not None:
+        d = np.abs(lse.cpu().double().numpy() - lse_ref)
+        assert np.all(d <= REL * (1 + np.abs(lse_ref))), f"{label}: lse {d.max():.3e}"
+
+
+SHAPES = [(1, 1), (3, 7), (5, 100), (7, 4096), (4, 8192), (4, 8193), (2, 20001), (3, 1 << 18)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_softmax_matches_oracle(dtype, dev):
+    for rows, n in SHAPES:
+        x = _inputs(rows, n, dtype, seed=rows * 7 + n)
+        print(f"softmax {dtype} rows={rows} n={n}", flush=True)
+        y, lse = iofa.softmax(x.to(dev), want_lse=True)
+        torch.cuda.synchronize()
+        _check(x, y, lse, f"{dtype} {rows}x{n}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_softmax_in_place_and_rows_sum_to_one(dtype, dev):
+    for rows, n in ((6, 3000), (3, 50000)):
+        x = _inputs(rows, n, dtype, seed=n)
+        xd = x.to(dev)
+        nbytes = iofa.fa_softmax_workspace_bytes(rows, n, xd.dtype)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+        iofa.fa_softmax_rows(xd, xd, None, ws)          # in place
+        torch.cuda.synchronize()
+        _check(x, xd, None, f"in place {dtype} {rows}x{n}")
+        s = xd.double().sum(dim=1).cpu().numpy()
+        assert np.abs(s - 1).max() <= (2e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_softmax_unaligned_rows_take_the_scalar_path(dev):
+    # a base one element past a 16-byte boundary and an odd row length
+    buf = _inputs(1, 5 * 9001 + 1, "bf16", seed=5).view(-1).to(dev)
+    x = buf[1:].view(5, 9001)
+    y = torch.empty_like(x)
+    lse = torch.empty(5, dtype=torch.float32, device=dev)
+    ws = torch.empty(iofa.fa_softmax_workspace_bytes(5, 9001, x.dtype), dtype=torch.uint8,
+                     device=dev)
+    iofa.fa_softmax_rows(x, y, lse, ws)
+    torch.cuda.synchronize()
+    _check(x.cpu(), y, lse, "unaligned bf16 5x9001")
+
+
+def test_softmax_stress_spread(dev):
+    # scores of the numerics-stress attention workload scale: spread about 16
+    for dtype in ("fp16", "bf16"):
+        x = _inputs(8, 8191, dtype, seed=99, spread=16.0)
+        y, lse = iofa.softmax(x.to(dev), want_lse=True)
+        torch.cuda.synchronize()
+        _check(x, y, lse, f"stress {dtype}")
