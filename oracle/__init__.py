@@ -14,7 +14,8 @@ Pages cited (titles/sections as printed on them):
            "Standard Attention", "增量求解 softmax" (also the block merge
            of partial attention results, merge.py).
   [xinc]   xinc.fun archive 235 -- sections "6. 标准注意力为什么慢",
-           "7. Online Softmax".
+           "7. Online Softmax" (also its closing remark on the backward
+           pass, backward.py).
 
 Every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` against something other than itself (brute
@@ -40,6 +41,7 @@ from .softmax import (
 from .tiled import tiled_online_attention
 from .mac_count import standard_attention_mac
 from .merge import merge_partials, partial_attention
+from .backward import attention_backward
 
 __all__ = [
     "decode_bf16",
@@ -56,4 +58,5 @@ __all__ = [
     "standard_attention_mac",
     "partial_attention",
     "merge_partials",
+    "attention_backward",
 ]

@@ -534,3 +534,86 @@ def test_online_row_stats_match_two_pass(n, block):
     m2, _, l2, _ = oracle.local_softmax(x)
     assert m == m2
     assert abs(l - l2) <= 1e-13 * l2
+
+
+# ----------------------------------------------------------------- backward
+
+def _loss_and_grads(q, k, v, do, scale):
+    # L = sum(O * dO): its gradient with respect to O is dO
+    o, _ = oracle.standard_attention(q, k, v, scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_against_central_differences(seed):
+    rng = np.random.default_rng(seed)
+    B, H, N, d = 1, 2, 6, 4
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    scale = 0.6
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = dict(q=q, k=k, v=v)
+            args_m = dict(q=q, k=k, v=v)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_loss_and_grads(args_p["q"], args_p["k"], args_p["v"], do, scale)
+                        - _loss_and_grads(args_m["q"], args_m["k"], args_m["v"], do, scale)) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-7 * max(1.0, np.abs(g).max()), name
+
+
+def test_backward_against_autograd():
+    rng = np.random.default_rng(7)
+    B, H, N, d = 2, 3, 33, 16
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    scale = 0.25
+    dq, dk, dv, D = oracle.attention_backward(q, k, v, do, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.softmax(scale * tq @ tk.transpose(-1, -2), dim=-1) @ tv
+    o.backward(torch.tensor(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.abs(mine - ref.numpy()).max() <= 1e-12 * max(1.0, np.abs(mine).max())
+    assert np.abs(D - (o.detach().numpy() * do).sum(-1)).max() <= 1e-12
+
+
+def test_backward_closed_forms():
+    rng = np.random.default_rng(8)
+    B, H, N, d = 1, 1, 20, 8
+    q, k, v = (rng.standard_normal((B, H, N, d)) for _ in range(3))
+    zero = oracle.attention_backward(q, k, v, np.zeros_like(q), 0.5)
+    assert all(np.all(g == 0) for g in zero[:3])
+    do = rng.standard_normal((B, H, N, d))
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.5)
+    # shifting every key by one vector leaves the output unchanged, so the
+    # key gradients sum to zero over the keys; the same holds for queries'
+    # effect on dV: dV rows sum to the column sums of dO (P rows sum to 1)
+    assert np.abs(dk.sum(axis=2)).max() <= 1e-12
+    assert np.abs(dv.sum(axis=2) - do.sum(axis=2)).max() <= 1e-12
+    # identical value rows: the output does not depend on Q or K
+    vc = np.broadcast_to(rng.standard_normal(d), v.shape).copy()
+    dq2, dk2, _, _ = oracle.attention_backward(q, k, vc, do, 0.5)
+    assert np.abs(dq2).max() <= 1e-12 and np.abs(dk2).max() <= 1e-12
+
+
+@pytest.mark.parametrize("kind", ["no_D", "no_scale", "transposed_ds"])
+def test_planted_backward_mistakes_fail_a_pin(kind):
+    import oracle.backward as ob
+    rng = np.random.default_rng(9)
+    q, k, v, do = (rng.standard_normal((1, 1, 12, 4)) for _ in range(4))
+    good = ob.attention_backward(q, k, v, do, 0.5)
+    s = 0.5 * (q[0, 0] @ k[0, 0].T)
+    p = np.exp(s - s.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    dp = do[0, 0] @ v[0, 0].T
+    D = (do[0, 0] * (p @ v[0, 0])).sum(1)
+    if kind == "no_D":
+        dq = 0.5 * (p * dp) @ k[0, 0]
+    elif kind == "no_scale":
+        dq = (p * (dp - D[:, None])) @ k[0, 0]
+    else:
+        dq = 0.5 * (p * (dp - D[:, None])).T @ k[0, 0]
+    assert np.abs(dq - good[0][0, 0]).max() > 1e-6
