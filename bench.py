@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-naive", action="store_true", help="skip the naive contrast")
     p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
     p.add_argument("--no-softmax", action="store_true", help="skip the row-softmax measurement")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -451,6 +452,28 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     }
 
 
+def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
+    """The backward pass on the same workload.  TFLOP/s on the algorithmic
+    count 10*B*H*N^2*d (the five N^2 d products a single pass needs, 2.5x the
+    forward's 4*B*H*N^2*d); the kernels recompute two more products, so they
+    execute 14*B*H*N^2*d."""
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = iofa.forward(qd, kd, vd, scale)
+    g = torch.Generator(device=dev).manual_seed(17)
+    do = torch.randn(qd.shape, generator=g, device=dev).to(qd.dtype)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(iofa.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+    steps = max(5, min(args.steps, 30))
+    _, ms = time_launches(lambda: iofa.fa_bwd(qd, kd, vd, o, do, lse, dq, dk, dv, ws, scale),
+                          steps, 3, torch)
+    alg = 10.0 * B * H * N * N * d
+    return {"workload": spec["name"], "ms": round(ms, 4),
+            "tflops_algorithmic": round(alg / (ms * 1e-3) / 1e12, 1),
+            "tflops_executed": round(1.4 * alg / (ms * 1e-3) / 1e12, 1),
+            "frac_of_peak_algorithmic": round(alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def softmax_measure(args, torch, iofa, dev):
     """The standalone row softmax on bf16 rows that fit one workgroup (x read
     once, y written once) and on long rows (x read twice).  Roofline: HBM;
@@ -596,6 +619,10 @@ def main():
     if not args.no_splitkv and spec["dtype"] != "fp32":
         line["splitkv_contrast"] = splitkv_contrast(spec, args, torch, iofa, dev)
         print(f"[bench] split-KV: {line['splitkv_contrast']}", file=sys.stderr, flush=True)
+
+    if not args.no_backward and spec["dtype"] != "fp32":
+        line["backward"] = backward_measure(q, k, v, scale, spec, args, torch, iofa, dev)
+        print(f"[bench] backward: {line['backward']}", file=sys.stderr, flush=True)
 
     if not args.no_softmax:
         line["softmax_rows"] = softmax_measure(args, torch, iofa, dev)

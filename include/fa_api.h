@@ -200,6 +200,36 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
  * than one chunk, else 0 (also for invalid arguments). */
 size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype);
 
+/*
+ * Backward pass of exact attention: dQ, dK, dV for an upstream gradient dO
+ * of O = softmax(scale * Q K^T) V, from Q, K, V, the forward's O and LSE.
+ * As xinc.fun archive 235, section "7. Online Softmax", closes: the scores
+ * are recomputed tile by tile from the saved inputs and the log-sum-exp,
+ * never read from a stored attention matrix:
+ *     P = exp(scale * Q K^T - LSE),   D = rowsum(dO * O),
+ *     dS = P * (dO V^T - D),   dV = P^T dO,
+ *     dQ = scale * dS K,   dK = scale * dS^T Q.
+ * 16-bit inputs only (FA_F16, FA_BF16; FA_F32 is FA_ERR_DTYPE): products on
+ * MFMA with fp32 accumulation, P and dS rounded to the input type for the
+ * products, outputs rounded (RNE) to the input type.  Deterministic (no
+ * atomics): dQ and dK/dV are computed by separate kernels, each recomputing
+ * the scores it needs.
+ *   Q, K, V, O, dO  in:  (B, H, N, d) `dtype`, 16-byte aligned; O and LSE as
+ *                        fa_fwd wrote them (for these Q, K, V and scale).
+ *   LSE             in:  (B, H, N) fp32.
+ *   dQ, dK, dV      out: (B, H, N, d) `dtype`, 16-byte aligned, overlapping
+ *                        no input, each other or the workspace.
+ *   workspace       caller-owned, fa_bwd_workspace_bytes(B, H, N) bytes,
+ *                   16-byte aligned; holds (LSE * log2 e, D) per row on return.
+ * Other arguments and errors as fa_fwd.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream);
+
+/* Workspace bytes of fa_bwd: B * H * N * 8 (0 for negative sizes). */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
+
 /* Bytes of ONE naive workspace (S or P): B * H * N * ldS * sizeof(dtype),
  * ldS = N rounded up to a multiple of 8.  Returns 0 for an invalid dtype
  * or negative sizes. */

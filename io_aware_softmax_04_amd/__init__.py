@@ -2,7 +2,7 @@
 
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_splitkv_num_splits``,
 ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
-``fa_softmax_workspace_bytes``, ``fa_naive_fwd``,
+``fa_softmax_workspace_bytes``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_naive_fwd``,
 ``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
 ``fa_version`` carry the names
 and meaning of the entry points declared in ``include/fa_api.h``; they only
@@ -26,6 +26,7 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
     "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "softmax",
+    "fa_bwd", "fa_bwd_workspace_bytes", "backward",
     "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
     "fa_last_error", "fa_version", "forward", "forward_splitkv", "naive_forward",
     "default_scale",
@@ -78,6 +79,11 @@ def load_library():
     lib.fa_softmax_rows.restype = ctypes.c_int
     lib.fa_softmax_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
     lib.fa_softmax_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, vp, ctypes.c_size_t,
+                           i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_naive_fwd.argtypes = [vp, vp, vp, vp, fp, vp, vp, i64, i64, i64, i64,
                                  ctypes.c_float, ctypes.c_int, vp]
     lib.fa_naive_fwd.restype = ctypes.c_int
@@ -227,6 +233,38 @@ def softmax(x, want_lse=False, stream=None):
     ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
     fa_softmax_rows(x, y, lse, ws, stream)
     return (y, lse) if want_lse else y
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace, scale, stream=None):
+    """Backward pass; writes dq, dk, dv in place.  workspace: byte tensor of
+    at least fa_bwd_workspace_bytes() bytes."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o)
+    for name, t in (("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q in shape and dtype and be contiguous")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 (B, H, N) tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _fptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, float(scale),
+                        _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+def fa_bwd_workspace_bytes(B, H, N):
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N))
+
+
+def backward(q, k, v, o, lse, do, scale=None, stream=None):
+    """Allocate dq, dk, dv and the workspace and run the backward pass."""
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(fa_bwd_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, scale, stream)
+    return dq, dk, dv
 
 
 def fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream=None):

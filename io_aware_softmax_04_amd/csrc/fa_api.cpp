@@ -280,6 +280,43 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
   return hip_status(iofa::launch_softmax(a), "softmax launch");
 }
 
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  if (B < 0 || H < 0 || N < 0) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N) * 2 * sizeof(float);
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+           int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  if (dtype == FA_F32) return fail(FA_ERR_DTYPE, "the backward pass takes FA_F16 or FA_BF16 inputs");
+  bool empty = false;
+  int st = check_common(Q, K, V, dQ, LSE, true, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!O || !dO || !dK || !dV) return fail(FA_ERR_NULL, "O, dO, dK and dV must not be NULL");
+  if (!aligned(O, 16) || !aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16))
+    return fail(FA_ERR_ALIGN, "O, dO, dK and dV must be 16-byte aligned");
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  if (!workspace) return fail(FA_ERR_NULL, "workspace must not be NULL");
+  if (!aligned(workspace, 16)) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_SHAPE, "workspace holds " + std::to_string(workspace_bytes) +
+                                  " bytes, the backward pass needs " + std::to_string(need));
+  const size_t tensor = static_cast<size_t>(B * H * N * d) * elem_bytes(dtype);
+  const size_t lse = static_cast<size_t>(B * H * N) * sizeof(float);
+  const Region in[6] = {{Q, tensor, "Q"}, {K, tensor, "K"}, {V, tensor, "V"},
+                        {O, tensor, "O"}, {dO, tensor, "dO"}, {LSE, lse, "LSE"}};
+  const Region out[4] = {{dQ, tensor, "dQ"}, {dK, tensor, "dK"}, {dV, tensor, "dV"},
+                         {workspace, need, "workspace"}};
+  st = check_aliasing(in, 6, out, 4);
+  if (st != FA_OK) return st;
+  if (iofa::bwd_workgroups(B * H, N) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, B * H, N, d, scale, dtype,
+                  static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_bwd(a), "backward launch");
+}
+
 size_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
   const int e = elem_bytes(dtype);
   if (e == 0 || B < 0 || H < 0 || N < 0) return 0;

@@ -1,0 +1,365 @@
+// Backward pass of exact attention for gfx950 (16-bit inputs).
+//
+// xinc.fun archive 235, section "7. Online Softmax", closes with the point
+// that the backward pass recomputes local scores from the saved inputs and a
+// few statistics instead of reading a stored attention matrix.  With the
+// forward's log-sum-exp L (natural log, scaled scores) every tile of
+// P = exp(scale * Q K^T - L) is rebuilt on chip, and for an upstream dO:
+//     D_i = sum_c dO_ic O_ic,   dS = P * (dO V^T - D),
+//     dV = P^T dO,   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Three kernels:
+//   bwd_stats    per row: (L * log2 e, D) into an fp32 pair workspace;
+//   bwd_dq       one workgroup per 128 query rows (4 waves x 32), K and V
+//                tiles of 32 keys streamed through LDS; per tile
+//                S^T = K Q^T, dP^T = V dO^T (both v_mfma_f32_32x32x16 with
+//                the lane owning a query column), P^T and dS^T in-lane,
+//                dQ^T += K^T dS^T with dS^T straight from registers and K^T
+//                read through ds_read_b64_tr_b16 -- the shape of the fused
+//                forward's P V;
+//   bwd_dkdv     one workgroup per 128 keys (4 waves x 32), Q and dO tiles
+//                of 32 queries (with their (L log2 e, D) pairs) streamed;
+//                per tile S = Q K^T and dP = dO V^T with the lane owning a
+//                key column (K and V fragments stay in registers), then
+//                dV^T += dO^T P and dK^T += Q^T dS with P, dS from registers
+//                and dO^T, Q^T through transposed reads.
+// dQ and dK recompute S and dP separately (7 products of N^2 d per head
+// against the 5 a single pass with atomic dQ updates would need) so that no
+// output is shared between workgroups and the result is deterministic.
+// Tiles that are read both as row fragments and transposed use the kv_swz
+// swizzle; copies are buffer_load ... lds into two stages, the next tile's
+// copies in flight while the current one is computed.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace iofa {
+
+namespace {
+
+constexpr int kBwdTile = 32;                 // keys (dq) / queries (dkdv) per tile
+constexpr int kBwdRows = 128;                // rows a workgroup owns (4 waves x 32)
+
+// ------------------------------------------------------------- stats pass
+
+// (L[r] * log2 e, D[r]) for every row r of B*H*N.  D/8 threads per row, each
+// 8 columns (16-byte loads).
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restrict__ O,
+                                                        const uint16_t* __restrict__ dO,
+                                                        const float* __restrict__ LSE,
+                                                        float2* __restrict__ stats, int64_t rows) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / TPR;
+  const int c8 = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (r < rows) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(O + r * D + 8 * c8);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * D + 8 * c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(T::to_f32(half_of(o, e)), T::to_f32(half_of(g, e)), acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, TPR);
+  if (r < rows && c8 == 0) stats[r] = make_float2(LSE[r] * kLog2e, acc);
+}
+
+// ------------------------------------------------------------ shared steps
+
+// Row-fragment product: acc (32 x 32) += A (32 rows of an LDS stage, all D
+// columns) times B (D x 32, per-lane fragments bf[kk]).  Lane (l32, hi)
+// reads row l32, chunk (2*kk + hi) of the kv_swz-swizzled stage.
+template <class T, int D>
+__device__ inline void rows_times(f32x16& acc, uint32_t stage, int l32, int hi,
+                                  const typename T::vec8 (&bf)[D / 16]) {
+  const int swz = kv_swz<D>(l32);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint32_t a = stage + static_cast<uint32_t>(l32 * D + (((2 * kk + hi) ^ swz) * 8)) * 2u;
+    acc = T::mfma(__builtin_bit_cast(typename T::vec8, lds_read16(a)), bf[kk], acc);
+  }
+}
+
+// Transposed-fragment product: out[cb] (32 columns c x 32) += A^T (columns
+// 32*cb.. of a kv_swz stage, rows = the product's k index) times the packed
+// B fragments pk[ks] (k-slot 8*hi + u of step ks holds tile row
+// 16*ks + 8*(u/4) + 4*hi + u%4, the order of an MFMA accumulator's rows).
+template <class T, int D>
+__device__ inline void cols_times(f32x16 (&out)[D / 32], uint32_t stage, int lane,
+                                  const typename T::vec8 (&pk)[2]) {
+  const int g = lane >> 4, t = lane & 15;
+  const int row = 4 * (g >> 1) + (t >> 2);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
+      const int r = 16 * ks + row;
+      const int chunk = (col >> 3) ^ kv_swz<D>(r);
+      const uint32_t a0 = stage + static_cast<uint32_t>(r * D + chunk * 8 + (col & 7)) * 2u;
+      const int chunk8 = (col >> 3) ^ kv_swz<D>(r + 8);
+      const uint32_t a1 = stage + static_cast<uint32_t>((r + 8) * D + chunk8 * 8 + (col & 7)) * 2u;
+      const s16x4 lo = lds_read_tr8(a0);
+      const s16x4 up = lds_read_tr8(a1);
+      const auto a = __builtin_bit_cast(typename T::vec8,
+                                        __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+      out[cb] = T::mfma(a, pk[ks], out[cb]);
+    }
+  }
+}
+
+// Pack 32 fp32 accumulator values (two 16-register halves) into the two
+// k-step B fragments of a product over the accumulator's rows.
+template <class T>
+__device__ inline void pack_b(const f32x16& v, typename T::vec8 (&pk)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = T::pack(v[8 * ks + 2 * e], v[8 * ks + 2 * e + 1]);
+    pk[ks] = __builtin_bit_cast(typename T::vec8, w);
+  }
+}
+
+// Stores a transposed accumulator out[cb] (lane = row of the output, its
+// registers = columns 32*cb + 8*g + 4*hi + 0..3) times `mul`, rounded.
+template <class T, int D>
+__device__ inline void store_rowmajor(uint16_t* dst, const f32x16 (&out)[D / 32], int hi, float mul) {
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = T::pack(out[cb][4 * g + 0] * mul, out[cb][4 * g + 1] * mul);
+      w[1] = T::pack(out[cb][4 * g + 2] * mul, out[cb][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2*>(dst + 32 * cb + 8 * g + 4 * hi) = w;
+    }
+  }
+}
+
+template <class T, int D>
+__device__ inline void load_row_frags(typename T::vec8 (&f)[D / 16], const uint16_t* row, bool valid,
+                                      int hi) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (valid) w = *reinterpret_cast<const u32x4*>(row + 16 * kk + 8 * hi);
+    f[kk] = __builtin_bit_cast(typename T::vec8, w);
+  }
+}
+
+// --------------------------------------------------------------- dQ kernel
+
+template <class T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float2* __restrict__ stats, uint16_t* __restrict__ dQ, int N, int num_qtiles,
+    int num_wg, float scale) {
+  using vec8 = typename T::vec8;
+  constexpr int BC = kBwdTile;
+  constexpr uint32_t TB = BC * D * 2u;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * BC * D];   // K0 K1 V0 V1
+  const uint32_t sm = lds_address(smem);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+
+  const int L = xcd_logical_id(blockIdx.x, num_wg);
+  const int bh = L / num_qtiles, qt = L % num_qtiles;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int q = qt * kBwdRows + wave * 32 + l32;
+  const bool qv = q < N;
+  TileCopy<D, BC, kSwzKV> kcp;
+  TileCopy<D, BC, kSwzKV> vcp;
+  kcp.init(wave, lane);
+  vcp.init(wave, lane);
+  const int NT = (N + BC - 1) / BC;
+  kcp.copy(K + head, 0, N, sm);
+  vcp.copy(V + head, 0, N, sm + 2 * TB);
+
+  vec8 qf[D / 16], df[D / 16];
+  load_row_frags<T, D>(qf, Q + head + static_cast<size_t>(q) * D, qv, hi);
+  load_row_frags<T, D>(df, dO + head + static_cast<size_t>(q) * D, qv, hi);
+  const float2 st = qv ? stats[static_cast<size_t>(bh) * N + q] : make_float2(0.f, 0.f);
+  const float lse2 = st.x, Dq = st.y;
+  const float c2 = scale * kLog2e;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
+
+  for (int j = 0; j < NT; ++j) {
+    const int P = j & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < NT) {
+      kcp.copy(K + head, (j + 1) * BC, N, sm + (1 - P) * TB);
+      vcp.copy(V + head, (j + 1) * BC, N, sm + (3 - P) * TB);
+    }
+    const uint32_t ks = sm + P * TB, vs = sm + (2 + P) * TB;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    rows_times<T, D>(s, ks, l32, hi, qf);    // S^T  (keys x queries)
+    rows_times<T, D>(dp, vs, l32, hi, df);   // dP^T
+    const int kvalid = N - j * BC;
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
+      float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
+      p = key < kvalid ? p : 0.f;
+      ds[r] = p * (dp[r] - Dq);
+    }
+    vec8 pk[2];
+    pack_b<T>(ds, pk);
+    cols_times<T, D>(acc, ks, lane, pk);     // dQ^T += K^T dS^T
+  }
+  if (qv) store_rowmajor<T, D>(dQ + head + static_cast<size_t>(q) * D, acc, hi, scale);
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ------------------------------------------------------------ dK/dV kernel
+
+// K and V fragments (2 x D/2 registers) plus the dK and dV accumulators
+// (2 x D registers) exceed the 256 registers of two workgroups per CU at
+// d = 128, so that instance runs one workgroup per CU.
+template <int D>
+constexpr int kDkdvOccupancy = D == 128 ? 1 : 2;
+
+template <class T, int D>
+__global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float2* __restrict__ stats, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+    int num_ktiles, int num_wg, float scale) {
+  using vec8 = typename T::vec8;
+  constexpr int BQ = kBwdTile;
+  constexpr uint32_t TB = BQ * D * 2u;
+  constexpr uint32_t SB = BQ * 8u;                       // (lse2, D) pairs of a tile
+  // Q0 Q1 dO0 dO1 (TB each), then stats 0, 1 (SB each)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(4 * TB + 2 * SB) / 2];
+  const uint32_t sm = lds_address(smem);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+
+  const int L = xcd_logical_id(blockIdx.x, num_wg);
+  const int bh = L / num_ktiles, kt = L % num_ktiles;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int key = kt * kBwdRows + wave * 32 + l32;
+  const bool kv = key < N;
+  TileCopy<D, BQ, kSwzKV> qcp;
+  TileCopy<D, BQ, kSwzKV> dcp;
+  qcp.init(wave, lane);
+  dcp.init(wave, lane);
+  const float2* sh = stats + static_cast<size_t>(bh) * N;
+  auto stats_copy = [&](int q0, uint32_t dst) {
+    if (wave == 0) {
+      const int rows = N - q0 > 0 ? N - q0 : 0;
+      const auto rsrc = buffer_rsrc(sh + q0, static_cast<uint32_t>(rows) * 8u);
+      lds_dma4(rsrc, static_cast<uint32_t>(lane) * 4u, dst);
+    }
+  };
+  const int NT = (N + BQ - 1) / BQ;
+  qcp.copy(Q + head, 0, N, sm);
+  dcp.copy(dO + head, 0, N, sm + 2 * TB);
+  stats_copy(0, sm + 4 * TB);
+
+  vec8 kf[D / 16], vf[D / 16];
+  load_row_frags<T, D>(kf, K + head + static_cast<size_t>(key) * D, kv, hi);
+  load_row_frags<T, D>(vf, V + head + static_cast<size_t>(key) * D, kv, hi);
+  const float c2 = scale * kLog2e;
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) dk[cb] = dv[cb] = f32x16{};
+
+  for (int j = 0; j < NT; ++j) {
+    const int P = j & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 < NT) {
+      qcp.copy(Q + head, (j + 1) * BQ, N, sm + (1 - P) * TB);
+      dcp.copy(dO + head, (j + 1) * BQ, N, sm + (3 - P) * TB);
+      stats_copy((j + 1) * BQ, sm + 4 * TB + (1 - P) * SB);
+    }
+    const uint32_t qs = sm + P * TB, ds_ = sm + (2 + P) * TB, ss = sm + 4 * TB + P * SB;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    rows_times<T, D>(s, qs, l32, hi, kf);    // S  (queries x keys)
+    rows_times<T, D>(dp, ds_, l32, hi, vf);  // dP
+    // this lane's 16 query rows: 8*g + 4*hi + 0..3 for g = 0..3
+    const int qvalid = N - j * BQ;
+    f32x16 p, dsv;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t a = ss + static_cast<uint32_t>(8 * g + 4 * hi) * 8u;
+      const u32x4 s01 = lds_read16(a), s23 = lds_read16(a + 16);   // (lse2, D) x 4
+      const float l2[4] = {__uint_as_float(s01[0]), __uint_as_float(s01[2]),
+                           __uint_as_float(s23[0]), __uint_as_float(s23[2])};
+      const float dd[4] = {__uint_as_float(s01[1]), __uint_as_float(s01[3]),
+                           __uint_as_float(s23[1]), __uint_as_float(s23[3])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        const int qi = 8 * g + 4 * hi + i;
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[i]));
+        pr = qi < qvalid ? pr : 0.f;
+        p[r] = pr;
+        dsv[r] = pr * (dp[r] - dd[i]);
+      }
+    }
+    vec8 pp[2], pd[2];
+    pack_b<T>(p, pp);
+    pack_b<T>(dsv, pd);
+    cols_times<T, D>(dv, ds_, lane, pp);     // dV^T += dO^T P
+    cols_times<T, D>(dk, qs, lane, pd);      // dK^T += Q^T dS
+  }
+  if (kv) {
+    store_rowmajor<T, D>(dK + head + static_cast<size_t>(key) * D, dk, hi, scale);
+    store_rowmajor<T, D>(dV + head + static_cast<size_t>(key) * D, dv, hi, 1.f);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+template <class T, int D>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+  const int64_t rows = a.BH * a.N;
+  {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t wg = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_stats_kernel<T, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+                       a.stream, static_cast<const uint16_t*>(a.O),
+                       static_cast<const uint16_t*>(a.dO), a.LSE, static_cast<float2*>(a.stats),
+                       rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int tiles = static_cast<int>((a.N + kBwdRows - 1) / kBwdRows);
+  const int64_t wg = a.BH * tiles;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+                     a.stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                     static_cast<const uint16_t*>(a.V), static_cast<const uint16_t*>(a.dO),
+                     static_cast<const float2*>(a.stats), static_cast<uint16_t*>(a.dQ),
+                     static_cast<int>(a.N), tiles, static_cast<int>(wg), a.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+                     a.stream, static_cast<const uint16_t*>(a.Q), static_cast<const uint16_t*>(a.K),
+                     static_cast<const uint16_t*>(a.V), static_cast<const uint16_t*>(a.dO),
+                     static_cast<const float2*>(a.stats), static_cast<uint16_t*>(a.dK),
+                     static_cast<uint16_t*>(a.dV), static_cast<int>(a.N), tiles,
+                     static_cast<int>(wg), a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_workgroups(int64_t BH, int64_t N) {
+  return BH * ((N + kBwdRows - 1) / kBwdRows);
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  if (a.dtype == kDtypeBF16) return a.d == 128 ? launch_bwd_t<Bf16, 128>(a) : launch_bwd_t<Bf16, 64>(a);
+  return a.d == 128 ? launch_bwd_t<F16, 128>(a) : launch_bwd_t<F16, 64>(a);
+}
+
+}  // namespace iofa

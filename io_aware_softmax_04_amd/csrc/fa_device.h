@@ -25,6 +25,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct Bf16 {
   using vec8 = bf16x8;
+  // fp32 value of the bf16 pattern in the low 16 bits of b
+  __device__ static inline float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
   }
@@ -39,6 +41,9 @@ struct Bf16 {
 
 struct F16 {
   using vec8 = f16x8;
+  __device__ static inline float to_f32(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+  }
   __device__ static inline uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
   }
@@ -207,6 +212,26 @@ __device__ inline int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// A tile read both ways -- 16-byte row fragments (16 consecutive rows, one
+// chunk) and ds_read_b64_tr_b16 (aligned groups of 4 rows, two adjacent
+// chunks) -- needs a swizzle whose 16 values over rows 0..15 are distinct
+// (row reads) and whose values shifted right by one are distinct within
+// every aligned group of 4 rows (transposed reads):
+//       chunk c of row r sits at c ^ (((r & 3) << 2) | ((r >> 2) & 3))          (D = 128)
+//                                c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))   (D = 64)
+template <int D>
+__device__ inline int kv_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// Swizzle selector of a tile copy: which of the layouts above.
+enum SwzKind { kSwzK = 0, kSwzV = 1, kSwzKV = 2 };
+template <int D>
+__device__ inline int tile_swz(int kind, int row) {
+  return kind == kSwzK ? k_swz<D>(row) : kind == kSwzV ? v_swz<D>(row) : kv_swz<D>(row);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define IOFA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -221,6 +246,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // from moving LDS accesses across it.
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_byte) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_byte)
+               : "memory");
+}
+// The same with 4 bytes per lane: 256 consecutive LDS bytes.
+__device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "{m0}"(lds_byte)
                : "memory");
@@ -248,12 +280,12 @@ __device__ inline void wait_vmem() {
 }
 
 // Per-lane part of the direct copies of one K or V tile (BC rows x D 16-bit
-// elements, row-major, chunks swizzled as above) from global memory into an
-// LDS stage by the NWV waves of a workgroup.  Wave w writes the 1 KiB blocks
+// elements, row-major, chunks swizzled by the SwzKind SWZ) from global
+// memory into an LDS stage by the NWV waves of a workgroup.  Wave w writes the 1 KiB blocks
 // b = w + NWV*i (i = 0 .. PER_WAVE-1); with this interleave the swizzle of
 // every row a lane copies is the same, and lane offsets differ between
 // blocks only by a constant.
-template <int D, int BC, bool IS_V, int NWV = 4>
+template <int D, int BC, int SWZ, int NWV = 4>
 struct TileCopy {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_BLK = 64 / CH;     // rows in one 1 KiB block
@@ -269,7 +301,7 @@ struct TileCopy {
   __device__ inline void init(int wave, int lane) {
     const int row0 = wave * ROWS_PER_BLK + lane / CH;
     const int p = lane % CH;
-    const int c = p ^ (IS_V ? v_swz<D>(row0) : k_swz<D>(row0));
+    const int c = p ^ tile_swz<D>(SWZ, row0);
     voff0 = static_cast<uint32_t>(row0 * D + 8 * c) * 2u;
     lds_wave = static_cast<uint32_t>(wave) * 1024u;
   }

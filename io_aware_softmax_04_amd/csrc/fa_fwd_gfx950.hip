@@ -325,8 +325,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
-  TileCopy<D, BC, false> kcp;
-  TileCopy<D, BC, true> vcp;
+  TileCopy<D, BC, kSwzK> kcp;
+  TileCopy<D, BC, kSwzV> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 

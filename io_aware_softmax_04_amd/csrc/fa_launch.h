@@ -64,6 +64,29 @@ struct SoftmaxArgs {
 int64_t softmax_chunk(int dtype);
 hipError_t launch_softmax(const SoftmaxArgs& a);
 
+// Backward pass (16-bit inputs): dQ, dK, dV from Q, K, V, O, dO and the
+// forward's LSE; stats: B*H*N float2 workspace of (LSE * log2 e, D).
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  void* stats;
+  int64_t BH;
+  int64_t N;
+  int64_t d;
+  float scale;
+  int dtype;
+  hipStream_t stream;
+};
+int64_t bwd_workgroups(int64_t BH, int64_t N);
+hipError_t launch_bwd(const BwdArgs& a);
+
 // Keys per tile and query rows per workgroup of the fused kernels.
 int fused_key_tile(int dtype, int64_t d);
 int64_t fused_query_tile(int dtype);

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
-        "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_naive_fwd",
+        "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_bwd",
+        "fa_bwd_workspace_bytes", "fa_naive_fwd",
         "fa_naive_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version"])
 
 
@@ -235,3 +236,39 @@ def test_softmax_in_place_and_empty_are_accepted_without_compute(lib):
     # in place, one chunk (no workspace), LSE elsewhere: passes validation;
     # the call would enqueue work, so only its rejection paths are tested here
     assert softmax_call(lib, y=Q + 2, x=Q) == 7
+
+
+# ------------------------------------------------------- backward (no GPU)
+
+DO_, DQ_, DK_, DV_ = (A * (20 + i) for i in range(4))
+
+
+def bwd(lib, o=O, do=DO_, dq=DQ_, dk=DK_, dv=DV_, ws=WS, ws_bytes=1 << 30, lse=L, **kw):
+    args = dict(q=Q, k=K, v=V, B=2, H=3, N=100, d=128, scale=0.1, dtype=2)
+    args.update(kw)
+    f = ctypes.cast(ctypes.c_void_p(lse), ctypes.POINTER(ctypes.c_float)) if lse else None
+    return lib.fa_bwd(*(ctypes.c_void_p(args[x]) for x in "qkv"), ctypes.c_void_p(o),
+                      ctypes.c_void_p(do), f, ctypes.c_void_p(dq), ctypes.c_void_p(dk),
+                      ctypes.c_void_p(dv), ctypes.c_void_p(ws), ws_bytes, args["B"], args["H"],
+                      args["N"], args["d"], args["scale"], args["dtype"], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert iofa.fa_bwd_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 8
+    assert iofa.fa_bwd_workspace_bytes(-1, 1, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), 4), (dict(dtype=3), 4), (dict(d=96), 3), (dict(N=-1), 2),
+    (dict(o=0), 1), (dict(do=0), 1), (dict(dk=0), 1), (dict(lse=0), 1), (dict(ws=0), 1),
+    (dict(ws_bytes=10), 2), (dict(dv=DV_ + 8), 5), (dict(ws=WS + 4), 5),
+    (dict(dq=Q), 7), (dict(dk=DQ_ + 32), 7), (dict(ws=DO_), 7), (dict(dv=O + 64), 7),
+    (dict(scale=float("nan")), 6),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, status):
+    st = bwd(lib, **kw)
+    assert st == status, (kw, st, iofa.fa_last_error())
+
+
+def test_bwd_empty_problem(lib):
+    assert bwd(lib, q=0, k=0, v=0, o=0, do=0, dq=0, dk=0, dv=0, ws=0, lse=0, N=0) == 0
