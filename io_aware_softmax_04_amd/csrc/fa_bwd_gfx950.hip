@@ -20,15 +20,17 @@
 //   bwd_dkdv     one workgroup per 128 keys (4 waves x 32), Q and dO tiles
 //                of 32 queries (with their (L log2 e, D) pairs) streamed;
 //                per tile S = Q K^T and dP = dO V^T with the lane owning a
-//                key column (K and V fragments stay in registers), then
-//                dV^T += dO^T P and dK^T += Q^T dS with P, dS from registers
-//                and dO^T, Q^T through transposed reads.
+//                key column (K fragments in registers, the workgroup's V
+//                rows resident in LDS), then dV^T += dO^T P and
+//                dK^T += Q^T dS with P, dS from registers and dO^T, Q^T
+//                through transposed reads.
 // dQ and dK recompute S and dP separately (7 products of N^2 d per head
 // against the 5 a single pass with atomic dQ updates would need) so that no
 // output is shared between workgroups and the result is deterministic.
 // Tiles that are read both as row fragments and transposed use the kv_swz
 // swizzle; copies are buffer_load ... lds into two stages, the next tile's
-// copies in flight while the current one is computed.
+// copies in flight while the current one is computed; the tile loop is
+// unrolled by two so stage offsets are immediates.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -67,43 +69,73 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restri
 
 // ------------------------------------------------------------ shared steps
 
-// Row-fragment product: acc (32 x 32) += A (32 rows of an LDS stage, all D
-// columns) times B (D x 32, per-lane fragments bf[kk]).  Lane (l32, hi)
-// reads row l32, chunk (2*kk + hi) of the kv_swz-swizzled stage.
-template <class T, int D>
-__device__ inline void rows_times(f32x16& acc, uint32_t stage, int l32, int hi,
-                                  const typename T::vec8 (&bf)[D / 16]) {
-  const int swz = kv_swz<D>(l32);
+// Per-lane LDS byte offsets (relative to a stage) of the two read patterns of
+// a kv_swz-swizzled tile of 32 rows, computed once so that every read in the
+// loop is a register plus an immediate (the stage offset).
+template <int D>
+struct LaneOffsets {
+  uint32_t row[D / 16];     // row fragment: row l32, chunk 2*kk + hi
+  uint32_t col[D / 32][2];  // transposed read: rows row0 (+8), columns 32*cb + ...
+
+  __device__ inline void init(int lane, int row_base) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int r = row_base + l32;
+    const int swz = kv_swz<D>(r);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const uint32_t a = stage + static_cast<uint32_t>(l32 * D + (((2 * kk + hi) ^ swz) * 8)) * 2u;
-    acc = T::mfma(__builtin_bit_cast(typename T::vec8, lds_read16(a)), bf[kk], acc);
+    for (int kk = 0; kk < D / 16; ++kk)
+      row[kk] = static_cast<uint32_t>(r * D + (((2 * kk + hi) ^ swz) * 8)) * 2u;
+    const int g = lane >> 4, t = lane & 15;
+    const int row0 = 4 * (g >> 1) + (t >> 2);
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int rr = row0 + 8 * h8;
+        const int c = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
+        const int chunk = (c >> 3) ^ kv_swz<D>(rr);
+        col[cb][h8] = static_cast<uint32_t>(rr * D + chunk * 8 + (c & 7)) * 2u;
+      }
   }
+};
+
+// Row-fragment product: acc (32 x 32) += A (32 rows of an LDS tile, all D
+// columns; lane (l32, hi) reads row l32, chunk 2*kk + hi) times B (D x 32,
+// per-lane fragments bf[kk]).
+template <class T, int D>
+__device__ inline void rows_times(f32x16& acc, uint32_t base, const LaneOffsets<D>& lo,
+                                  const typename T::vec8 (&bf)[D / 16]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    acc = T::mfma(__builtin_bit_cast(typename T::vec8, lds_read16(base + lo.row[kk])), bf[kk], acc);
+}
+
+// The same product with B's fragments read from another LDS tile of the same
+// layout (lane (l32, hi) holds row l32, columns 16*kk + 8*hi .. +7), one
+// k-step at a time so that no whole operand is held in registers.
+template <class T, int D>
+__device__ inline void rows_times_lds(f32x16& acc, uint32_t abase, uint32_t bbase,
+                                      const LaneOffsets<D>& lo) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    acc = T::mfma(__builtin_bit_cast(typename T::vec8, lds_read16(abase + lo.row[kk])),
+                  __builtin_bit_cast(typename T::vec8, lds_read16(bbase + lo.row[kk])), acc);
 }
 
 // Transposed-fragment product: out[cb] (32 columns c x 32) += A^T (columns
-// 32*cb.. of a kv_swz stage, rows = the product's k index) times the packed
-// B fragments pk[ks] (k-slot 8*hi + u of step ks holds tile row
+// 32*cb.. of a 32-row LDS tile, rows = the product's k index) times the
+// packed B fragments pk[ks] (k-slot 8*hi + u of step ks holds tile row
 // 16*ks + 8*(u/4) + 4*hi + u%4, the order of an MFMA accumulator's rows).
 template <class T, int D>
-__device__ inline void cols_times(f32x16 (&out)[D / 32], uint32_t stage, int lane,
+__device__ inline void cols_times(f32x16 (&out)[D / 32], uint32_t base, const LaneOffsets<D>& lo,
                                   const typename T::vec8 (&pk)[2]) {
-  const int g = lane >> 4, t = lane & 15;
-  const int row = 4 * (g >> 1) + (t >> 2);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int cb = 0; cb < D / 32; ++cb) {
-      const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
-      const int r = 16 * ks + row;
-      const int chunk = (col >> 3) ^ kv_swz<D>(r);
-      const uint32_t a0 = stage + static_cast<uint32_t>(r * D + chunk * 8 + (col & 7)) * 2u;
-      const int chunk8 = (col >> 3) ^ kv_swz<D>(r + 8);
-      const uint32_t a1 = stage + static_cast<uint32_t>((r + 8) * D + chunk8 * 8 + (col & 7)) * 2u;
-      const s16x4 lo = lds_read_tr8(a0);
-      const s16x4 up = lds_read_tr8(a1);
+      const s16x4 lo4 = lds_read_tr8(base + lo.col[cb][0] + 16 * ks * D * 2);
+      const s16x4 up4 = lds_read_tr8(base + lo.col[cb][1] + 16 * ks * D * 2);
       const auto a = __builtin_bit_cast(typename T::vec8,
-                                        __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+                                        __builtin_shufflevector(lo4, up4, 0, 1, 2, 3, 4, 5, 6, 7));
       out[cb] = T::mfma(a, pk[ks], out[cb]);
     }
   }
@@ -149,6 +181,9 @@ __device__ inline void load_row_frags(typename T::vec8 (&f)[D / 16], const uint1
   }
 }
 
+using P0 = std::integral_constant<int, 0>;
+using P1 = std::integral_constant<int, 1>;
+
 // --------------------------------------------------------------- dQ kernel
 
 template <class T, int D>
@@ -175,6 +210,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   TileCopy<D, BC, kSwzKV> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
+  LaneOffsets<D> lo;
+  lo.init(lane, 0);
   const int NT = (N + BC - 1) / BC;
   kcp.copy(K + head, 0, N, sm);
   vcp.copy(V + head, 0, N, sm + 2 * TB);
@@ -189,18 +226,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
 
-  for (int j = 0; j < NT; ++j) {
-    const int P = j & 1;
+  // tile j in stage j % 2; the copies of tile j+1 are in flight meanwhile
+  auto tile = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < NT) {
       kcp.copy(K + head, (j + 1) * BC, N, sm + (1 - P) * TB);
       vcp.copy(V + head, (j + 1) * BC, N, sm + (3 - P) * TB);
     }
-    const uint32_t ks = sm + P * TB, vs = sm + (2 + P) * TB;
     f32x16 s = f32x16{}, dp = f32x16{};
-    rows_times<T, D>(s, ks, l32, hi, qf);    // S^T  (keys x queries)
-    rows_times<T, D>(dp, vs, l32, hi, df);   // dP^T
+    rows_times<T, D>(s, sm + P * TB, lo, qf);          // S^T  (keys x queries)
+    rows_times<T, D>(dp, sm + (2 + P) * TB, lo, df);   // dP^T
     const int kvalid = N - j * BC;
     f32x16 ds;
 #pragma unroll
@@ -212,22 +249,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     vec8 pk[2];
     pack_b<T>(ds, pk);
-    cols_times<T, D>(acc, ks, lane, pk);     // dQ^T += K^T dS^T
+    cols_times<T, D>(acc, sm + P * TB, lo, pk);        // dQ^T += K^T dS^T
+  };
+  int j = 0;
+  for (; j + 1 < NT; j += 2) {
+    tile(P0{}, j);
+    tile(P1{}, j + 1);
   }
+  if (j < NT) tile(P0{}, j);
   if (qv) store_rowmajor<T, D>(dQ + head + static_cast<size_t>(q) * D, acc, hi, scale);
   __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ------------------------------------------------------------ dK/dV kernel
 
-// K and V fragments (2 x D/2 registers) plus the dK and dV accumulators
-// (2 x D registers) exceed the 256 registers of two workgroups per CU at
-// d = 128, so that instance runs one workgroup per CU.
-template <int D>
-constexpr int kDkdvOccupancy = D == 128 ? 1 : 2;
-
 template <class T, int D>
-__global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float2* __restrict__ stats, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
@@ -236,9 +273,11 @@ __global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
   constexpr int BQ = kBwdTile;
   constexpr uint32_t TB = BQ * D * 2u;
   constexpr uint32_t SB = BQ * 8u;                       // (lse2, D) pairs of a tile
-  // Q0 Q1 dO0 dO1 (TB each), then stats 0, 1 (SB each)
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[(4 * TB + 2 * SB) / 2];
+  constexpr uint32_t VB = kBwdRows * D * 2u;             // the workgroup's V rows
+  // Q0 Q1 dO0 dO1 (TB each), stats 0, 1 (SB each), then V (VB)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(4 * TB + 2 * SB + VB) / 2];
   const uint32_t sm = lds_address(smem);
+  const uint32_t vbase = sm + 4 * TB + 2 * SB;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -246,12 +285,18 @@ __global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
   const int L = xcd_logical_id(blockIdx.x, num_wg);
   const int bh = L / num_ktiles, kt = L % num_ktiles;
   const size_t head = static_cast<size_t>(bh) * N * D;
-  const int key = kt * kBwdRows + wave * 32 + l32;
+  const int k0 = kt * kBwdRows;
+  const int key = k0 + wave * 32 + l32;
   const bool kv = key < N;
   TileCopy<D, BQ, kSwzKV> qcp;
   TileCopy<D, BQ, kSwzKV> dcp;
   qcp.init(wave, lane);
   dcp.init(wave, lane);
+  LaneOffsets<D> lo;
+  lo.init(lane, 0);
+  // this wave's 32 V rows; kv_swz depends on the row modulo 16 only, so the
+  // offsets of a 32-row tile serve them
+  const uint32_t vwave = vbase + static_cast<uint32_t>(wave) * 32u * D * 2u;
   const float2* sh = stats + static_cast<size_t>(bh) * N;
   auto stats_copy = [&](int q0, uint32_t dst) {
     if (wave == 0) {
@@ -261,20 +306,24 @@ __global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
     }
   };
   const int NT = (N + BQ - 1) / BQ;
+  {
+    TileCopy<D, kBwdRows, kSwzKV> vcp;                   // the workgroup's 128 V rows, once
+    vcp.init(wave, lane);
+    vcp.copy(V + head, k0, N, vbase);
+  }
   qcp.copy(Q + head, 0, N, sm);
   dcp.copy(dO + head, 0, N, sm + 2 * TB);
   stats_copy(0, sm + 4 * TB);
 
-  vec8 kf[D / 16], vf[D / 16];
+  vec8 kf[D / 16];
   load_row_frags<T, D>(kf, K + head + static_cast<size_t>(key) * D, kv, hi);
-  load_row_frags<T, D>(vf, V + head + static_cast<size_t>(key) * D, kv, hi);
   const float c2 = scale * kLog2e;
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) dk[cb] = dv[cb] = f32x16{};
 
-  for (int j = 0; j < NT; ++j) {
-    const int P = j & 1;
+  auto tile = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < NT) {
@@ -282,10 +331,10 @@ __global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
       dcp.copy(dO + head, (j + 1) * BQ, N, sm + (3 - P) * TB);
       stats_copy((j + 1) * BQ, sm + 4 * TB + (1 - P) * SB);
     }
-    const uint32_t qs = sm + P * TB, ds_ = sm + (2 + P) * TB, ss = sm + 4 * TB + P * SB;
+    const uint32_t qs = sm + P * TB, dos = sm + (2 + P) * TB, ss = sm + 4 * TB + P * SB;
     f32x16 s = f32x16{}, dp = f32x16{};
-    rows_times<T, D>(s, qs, l32, hi, kf);    // S  (queries x keys)
-    rows_times<T, D>(dp, ds_, l32, hi, vf);  // dP
+    rows_times<T, D>(s, qs, lo, kf);         // S  (queries x keys)
+    rows_times_lds<T, D>(dp, dos, vwave, lo);  // dP
     // this lane's 16 query rows: 8*g + 4*hi + 0..3 for g = 0..3
     const int qvalid = N - j * BQ;
     f32x16 p, dsv;
@@ -310,9 +359,15 @@ __global__ __launch_bounds__(256, kDkdvOccupancy<D>) void bwd_dkdv_kernel(
     vec8 pp[2], pd[2];
     pack_b<T>(p, pp);
     pack_b<T>(dsv, pd);
-    cols_times<T, D>(dv, ds_, lane, pp);     // dV^T += dO^T P
-    cols_times<T, D>(dk, qs, lane, pd);      // dK^T += Q^T dS
+    cols_times<T, D>(dv, dos, lo, pp);       // dV^T += dO^T P
+    cols_times<T, D>(dk, qs, lo, pd);        // dK^T += Q^T dS
+  };
+  int j = 0;
+  for (; j + 1 < NT; j += 2) {
+    tile(P0{}, j);
+    tile(P1{}, j + 1);
   }
+  if (j < NT) tile(P0{}, j);
   if (kv) {
     store_rowmajor<T, D>(dK + head + static_cast<size_t>(key) * D, dk, hi, scale);
     store_rowmajor<T, D>(dV + head + static_cast<size_t>(key) * D, dv, hi, 1.f);
