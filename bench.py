@@ -92,6 +92,19 @@ def bytes_models(spec, br=128):
     }
 
 
+def fused_grid_items(spec, br=128, threads=256):
+    """Work-items of the fused kernel's launch at the workload (its grid as
+    the profiler reports it), which tells its dispatches apart from launches
+    of the same kernel on other shapes in the same run (the split-KV
+    contrast's head share)."""
+    return spec["B"] * spec["H"] * math.ceil(spec["N"] / br) * threads
+
+
+def _is_fused(row, spec, grid_key="Grid_Size"):
+    return (FUSED_KERNEL_NAME in row["Kernel_Name"] and ", false>" in row["Kernel_Name"]
+            and int(row[grid_key]) == fused_grid_items(spec))
+
+
 def _counter_rows(directory, counter):
     import csv
     import glob
@@ -113,7 +126,7 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
     out = {}
     for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(directory, counter)
-        fused = [float(r["Counter_Value"]) for r in rows if FUSED_KERNEL_NAME in r["Kernel_Name"]]
+        fused = [float(r["Counter_Value"]) for r in rows if _is_fused(r, spec)]
         copy = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_NAME in r["Kernel_Name"]]
         if not fused or not copy:
             raise SystemExit(f"{counter}: fused or calibration-copy dispatches missing")
@@ -206,15 +219,20 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
 
 
 def summarise_trace(trace_dir, index, spec, bench_args):
-    """Per-kernel durations from rocprofv3's kernel_stats.csv, with the
-    fused kernel's rate at the algorithmic FLOP count."""
+    """Per-kernel durations from rocprofv3's kernel_trace.csv, one row per
+    kernel and launch grid, with the fused kernel's rate at the algorithmic
+    FLOP count for the workload's grid."""
     import csv
     import glob
-    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
-        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    groups = {}
     with open(files[0], encoding="utf-8") as fh:
-        rows = list(csv.DictReader(fh))
+        for r in csv.DictReader(fh):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"])
+                   * int(r["Grid_Size_Z"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     flops = 4.0 * spec["B"] * spec["H"] * spec["N"] ** 2 * spec["d"]
     tag = workload_tag(spec)
     lines = [
@@ -228,18 +246,23 @@ def summarise_trace(trace_dir, index, spec, bench_args):
         f"python bench.py --workload {index} --trace-from {trace_dir} --trace-cmd '{bench_args}'",
         "```",
         "",
-        "| kernel | calls | average (ns) | min (ns) | max (ns) | TFLOP/s at 4BHN^2d |",
-        "|---|---|---|---|---|---|",
+        f"One row per kernel and launch grid (work-items); the fused forward at this "
+        f"workload launches {fused_grid_items(spec)} work-items, other grids of the same "
+        f"kernel belong to the split-KV contrast's head share.",
+        "",
+        "| kernel | grid | calls | average (ns) | min (ns) | max (ns) | TFLOP/s at 4BHN^2d |",
+        "|---|---|---|---|---|---|---|",
     ]
-    for r in rows:
-        name = r["Name"]
+    for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         short = name.replace("(anonymous namespace)::", "").split("(")[0]
         short = short.replace("void ", "").replace("iofa::", "")
+        if short.startswith("at::native"):
+            short = short.split("<")[0]
         rate = ""
-        if FUSED_KERNEL_NAME in name:
-            rate = f"{flops / (float(r['AverageNs']) * 1e-9) / 1e12:.1f}"
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | {rate} |")
+        if _is_fused({"Kernel_Name": name, "Grid_Size": grid}, spec):
+            rate = f"{flops / (sum(ns) / len(ns) * 1e-9) / 1e12:.1f}"
+        lines.append(f"| {short} | {grid} | {len(ns)} | {sum(ns) / len(ns):.0f} | {min(ns)} | "
+                     f"{max(ns)} | {rate} |")
     lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
     path = os.path.join(ROOT, f"profiles/kernel_trace_{tag}.md")
     with open(path, "w", encoding="utf-8") as fh:
@@ -271,7 +294,7 @@ def summarise_sq(pmc_dir, index, spec):
     for f in files:
         with open(f, encoding="utf-8") as fh:
             for r in csv.DictReader(fh):
-                if FUSED_KERNEL_NAME not in r["Kernel_Name"]:
+                if not _is_fused(r, spec):
                     continue
                 d = per.setdefault(int(r["Dispatch_Id"]), {})
                 d[r["Counter_Name"]] = float(r["Counter_Value"])
