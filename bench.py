@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd attention TFLOP/s (4BHN²d/t) + % bf16 MFMA peak, N=4096 d=128"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 FUSED_KERNEL_SOURCES = ["io_aware_softmax_04_amd/csrc/fa_fwd_gfx950.hip",
                         "io_aware_softmax_04_amd/csrc/fa_device.h"]
@@ -44,6 +45,7 @@ def parse():
     p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
     p.add_argument("--no-softmax", action="store_true", help="skip the row-softmax measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -497,6 +499,27 @@ def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
             "frac_of_peak_algorithmic": round(alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def fp8_measure(spec, args, torch, iofa, dev):
+    """The FP8 (E4M3) forward on the workload's shape: inputs from
+    make_qkv_fp8 (per-tensor scales), output bf16.  TFLOP/s at 4*B*H*N^2*d
+    against the dense fp8 MFMA peak."""
+    from workloads import make_qkv_fp8, default_scale
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(B, H, N, d, seed_base=1000 * args.workload)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    scale = default_scale(d)
+    steps = max(5, min(args.steps, 50))
+    _, ms = time_launches(lambda: iofa.fa_fwd_fp8(q8, k8, v8, o, lse, scale, sq, sk, sv),
+                          steps, min(args.warmup, 5), torch)
+    tf = 4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12
+    return {"workload": f"fp8 (E4M3, per-tensor scales) B{B} H{H} N{N} d{d}, bf16 output",
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
+
+
 def softmax_measure(args, torch, iofa, dev):
     """The standalone row softmax on bf16 rows that fit one workgroup (x read
     once, y written once) and on long rows (x read twice).  Roofline: HBM;
@@ -646,6 +669,10 @@ def main():
     if not args.no_backward and spec["dtype"] != "fp32":
         line["backward"] = backward_measure(q, k, v, scale, spec, args, torch, iofa, dev)
         print(f"[bench] backward: {line['backward']}", file=sys.stderr, flush=True)
+
+    if not args.no_fp8 and spec["dtype"] != "fp32":
+        line["fp8_forward"] = fp8_measure(spec, args, torch, iofa, dev)
+        print(f"[bench] fp8 forward: {line['fp8_forward']}", file=sys.stderr, flush=True)
 
     if not args.no_softmax:
         line["softmax_rows"] = softmax_measure(args, torch, iofa, dev)

@@ -92,6 +92,39 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
            void* stream);
 
 /*
+ * FP8 fused forward: fa_fwd's result for inputs held as 8-bit floats.
+ *
+ * Section "4. 减少访存的几种办法" of the xinc.fun archive 235 page lets the
+ * matrix products run on FP8 operands while accumulation, softmax and
+ * normalisation keep a wider format; this entry point does that with the
+ * online-softmax recurrence of fa_fwd.  Q, K, V hold OCP FP8 E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+ * value 448; codes 0x7F and 0xFF are NaN) and each tensor has one fp32
+ * scale: element x of Q stands for q_scale * e4m3(x), likewise K and V.
+ * The result is
+ *     O   = softmax(scale * (q_scale Q)(k_scale K)^T) (v_scale V)
+ *     LSE = ln sum_j exp(scale * q_scale * k_scale * q_i . k_j)
+ * with the scores accumulated in fp32 from exact code products, the
+ * softmax in fp32, the probabilities rounded to E4M3 (nearest-even) for the
+ * P V product with fp32 accumulation, and O rounded to bf16 (nearest-even).
+ *
+ *   Q, K, V  in:  (B, H, N, d) E4M3 codes (one byte each), 16-byte aligned,
+ *                 finite codes only.
+ *   O        out: (B, H, N, d) bf16, 16-byte aligned; must not overlap
+ *                 Q, K, V or LSE.
+ *   LSE      out: (B, H, N) fp32, 4-byte aligned, required; must not
+ *                 overlap Q, K, V or O.
+ *   scale    finite fp32 multiplier of the scores (1/sqrt(d) usually).
+ *   q_scale, k_scale, v_scale
+ *            finite and > 0 (FA_ERR_SCALE otherwise); |scale| * q_scale *
+ *            k_scale must also be finite in fp32.
+ * Other conventions (shapes, limits, stream, errors) as fa_fwd.
+ */
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+               float q_scale, float k_scale, float v_scale, void* stream);
+
+/*
  * Naive three-kernel forward, kept as the measured contrast of the ctyun.cn
  * article's "MAC分析 / 标准Transformer MAC分析" (and of the three-step
  * listing in section "Standard Attention" of the special-jiahao.github.io

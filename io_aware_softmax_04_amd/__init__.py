@@ -2,7 +2,8 @@
 
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_splitkv_num_splits``,
 ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
-``fa_softmax_workspace_bytes``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_naive_fwd``,
+``fa_softmax_workspace_bytes``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_fp8``,
+``fa_naive_fwd``,
 ``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
 ``fa_version`` carry the names
 and meaning of the entry points declared in ``include/fa_api.h``; they only
@@ -10,7 +11,7 @@ marshal torch tensors into pointers, sizes and the current HIP stream.  Every
 step of the computation runs in the HIP kernels of ``libiofa.so``; there is
 no CPU fallback, and a missing library raises instead of computing.
 
-``forward``, ``forward_splitkv`` and ``naive_forward`` are conveniences
+``forward``, ``forward_splitkv``, ``forward_fp8`` and ``naive_forward`` are conveniences
 that allocate the outputs (and workspaces) with torch and call the entry
 points.
 """
@@ -26,7 +27,7 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
     "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "softmax",
-    "fa_bwd", "fa_bwd_workspace_bytes", "backward",
+    "fa_bwd", "fa_bwd_workspace_bytes", "backward", "fa_fwd_fp8", "forward_fp8",
     "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
     "fa_last_error", "fa_version", "forward", "forward_splitkv", "naive_forward",
     "default_scale",
@@ -66,6 +67,9 @@ def load_library():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, fp, i64, i64, i64, i64, ctypes.c_float,
+                               ctypes.c_float, ctypes.c_float, ctypes.c_float, vp]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                    i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
@@ -147,6 +151,33 @@ def fa_fwd(q, k, v, o, lse, scale, stream=None):
     with torch.cuda.device(q.device):
         st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), B, H, N, d,
                         float(scale), _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+_FP8_INPUT = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, scale, q_scale, k_scale, v_scale, stream=None):
+    """FP8 forward: q, k, v are (B, H, N, d) E4M3 codes (uint8 or
+    float8_e4m3fn tensors, same shape), o a bf16 tensor of that shape and
+    lse a (B, H, N) fp32 tensor, written in place."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype not in _FP8_INPUT:
+            raise ValueError(f"{name} must be a contiguous (B, H, N, d) uint8 or "
+                             "float8_e4m3fn tensor")
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape and device")
+    if o.dtype != torch.bfloat16 or o.shape != q.shape or not o.is_contiguous():
+        raise ValueError("o must be a contiguous bf16 tensor of q's shape")
+    B, H, N, d = (int(x) for x in q.shape)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous fp32 (B, H, N) tensor")
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse), B, H, N, d,
+                            float(scale), float(q_scale), float(k_scale), float(v_scale),
+                            _stream(stream, q.device))
     _check(st)
 
 
@@ -314,6 +345,17 @@ def forward(q, k, v, scale=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale, stream)
+    return o, lse
+
+
+def forward_fp8(q, k, v, q_scale, k_scale, v_scale, scale=None, stream=None):
+    """Allocate O (bf16) and LSE and run the FP8 forward on E4M3 codes.
+    Returns (o, lse)."""
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, o, lse, scale, q_scale, k_scale, v_scale, stream)
     return o, lse
 
 

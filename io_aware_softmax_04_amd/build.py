@@ -21,7 +21,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libiofa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd_gfx950.hip", "fa_naive_gfx950.hip", "fa_merge_gfx950.hip",
-           "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip"]
+           "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip", "fa_fwd_fp8_gfx950.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -119,6 +119,35 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   return hip_status(iofa::launch_fused(a), "fused forward launch");
 }
 
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+               int64_t H, int64_t N, int64_t d, float scale, float q_scale, float k_scale,
+               float v_scale, void* stream) {
+  g_last_error.clear();
+  const float ts[3] = {q_scale, k_scale, v_scale};
+  const char* tn[3] = {"q_scale", "k_scale", "v_scale"};
+  for (int i = 0; i < 3; ++i)
+    if (!(std::isfinite(ts[i]) && ts[i] > 0.f))
+      return fail(FA_ERR_SCALE, std::string(tn[i]) + " must be finite and > 0");
+  // shape, head-dimension, scale, pointer and alignment checks of a 16-bit call
+  bool empty = false;
+  int st = check_common(Q, K, V, O, LSE, true, B, H, N, d, scale, FA_BF16, &empty);
+  if (st != FA_OK || empty) return st;
+  const double c2 = std::fabs(static_cast<double>(scale)) * q_scale * k_scale * 1.4426950408889634;
+  if (!std::isfinite(static_cast<float>(c2)))
+    return fail(FA_ERR_SCALE, "|scale| * q_scale * k_scale overflows fp32");
+  const size_t codes = static_cast<size_t>(B * H * N * d);
+  const size_t lse = static_cast<size_t>(B * H * N) * sizeof(float);
+  const Region in[3] = {{Q, codes, "Q"}, {K, codes, "K"}, {V, codes, "V"}};
+  const Region out[2] = {{O, codes * 2, "O"}, {LSE, lse, "LSE"}};
+  st = check_aliasing(in, 3, out, 2);
+  if (st != FA_OK) return st;
+  if (iofa::fp8_workgroups(B * H, N) >= (int64_t(1) << 31))
+    return fail(FA_ERR_SHAPE, "too many workgroups");
+  iofa::Fp8Args a{Q, K, V, O, LSE, B * H, N, d, static_cast<float>(c2), v_scale, scale < 0.f,
+                  static_cast<hipStream_t>(stream)};
+  return hip_status(iofa::launch_fp8(a), "FP8 forward launch");
+}
+
 int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested) {
   if (elem_bytes(dtype) == 0 || B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   const int64_t tiles = (N + iofa::fused_key_tile(dtype, d) - 1) / iofa::fused_key_tile(dtype, d);
@@ -341,6 +370,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 }  // extern "C"

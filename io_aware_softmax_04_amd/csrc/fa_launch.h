@@ -87,6 +87,24 @@ struct BwdArgs {
 int64_t bwd_workgroups(int64_t BH, int64_t N);
 hipError_t launch_bwd(const BwdArgs& a);
 
+// FP8 (E4M3) forward: Q, K, V codes (B*H, N, d), O bf16, LSE fp32.
+struct Fp8Args {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int64_t BH;
+  int64_t N;
+  int64_t d;
+  float c2;        // |scale| * q_scale * k_scale * log2(e)
+  float v_scale;
+  bool negate_q;   // scale < 0: Q's signs are flipped on load
+  hipStream_t stream;
+};
+int64_t fp8_workgroups(int64_t BH, int64_t N);
+hipError_t launch_fp8(const Fp8Args& a);
+
 // Keys per tile and query rows per workgroup of the fused kernels.
 int fused_key_tile(int dtype, int64_t d);
 int64_t fused_query_tile(int dtype);

@@ -15,7 +15,8 @@ Pages cited (titles/sections as printed on them):
            of partial attention results, merge.py).
   [xinc]   xinc.fun archive 235 -- sections "6. 标准注意力为什么慢",
            "7. Online Softmax" (also its closing remark on the backward
-           pass, backward.py).
+           pass, backward.py), "4. 减少访存的几种办法" (FP8 matrix-product
+           inputs, fp8.py).
 
 Every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` against something other than itself (brute
@@ -42,6 +43,7 @@ from .tiled import tiled_online_attention
 from .mac_count import standard_attention_mac
 from .merge import merge_partials, partial_attention
 from .backward import attention_backward
+from .fp8 import decode_e4m3, fp8_attention, fp8_attention_rows, fp8_values
 
 __all__ = [
     "decode_bf16",
@@ -59,4 +61,8 @@ __all__ = [
     "partial_attention",
     "merge_partials",
     "attention_backward",
+    "decode_e4m3",
+    "fp8_values",
+    "fp8_attention",
+    "fp8_attention_rows",
 ]

@@ -25,14 +25,14 @@ def lib():
 def declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
         "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_bwd",
-        "fa_bwd_workspace_bytes", "fa_naive_fwd",
+        "fa_bwd_workspace_bytes", "fa_fwd_fp8", "fa_naive_fwd",
         "fa_naive_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version"])
 
 
@@ -44,12 +44,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_symbols_have_c_linkage():
     out = os.popen(f"nm -D --defined-only {iofa.library_path()}").read()
-    exported = set(re.findall(r"\bT (fa_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (fa_[a-z0-9_]+)\b", out))
     assert set(declared_functions()) <= exported
 
 
 def test_status_strings_and_version(lib):
-    assert iofa.fa_version() == 200
+    assert iofa.fa_version() == 300
     assert iofa.fa_status_string(0) == "ok"
     for s in range(1, 9):
         assert iofa.fa_status_string(s) not in ("ok", "unknown status")
@@ -272,3 +272,41 @@ def test_bwd_rejects_bad_arguments(lib, kw, status):
 
 def test_bwd_empty_problem(lib):
     assert bwd(lib, q=0, k=0, v=0, o=0, do=0, dq=0, dk=0, dv=0, ws=0, lse=0, N=0) == 0
+
+
+# ------------------------------------------------------- FP8 forward (no GPU)
+
+def fp8(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=128, scale=0.1, sq=0.01,
+        sk=0.02, sv=0.5):
+    f = ctypes.cast(ctypes.c_void_p(lse), ctypes.POINTER(ctypes.c_float)) if lse else None
+    return lib.fa_fwd_fp8(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v),
+                          ctypes.c_void_p(o), f, B, H, N, d, scale, sq, sk, sv, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), 3), (dict(N=-1), 2), (dict(B=1 << 16, H=1 << 16), 2),
+    (dict(scale=float("nan")), 6), (dict(sq=0.0), 6), (dict(sk=-1.0), 6),
+    (dict(sv=float("inf")), 6), (dict(sq=float("nan")), 6),
+    (dict(scale=1e30, sq=1e10, sk=1e10), 6),     # the score multiplier overflows fp32
+    (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(v=V + 8), 5), (dict(o=O + 2), 5), (dict(lse=L + 2), 5),
+    (dict(o=Q), 7), (dict(lse=O + 2 * 2 * 3 * 100 * 128 - 16), 7),
+    (dict(o=K - 2 * 2 * 3 * 100 * 128 + 16), 7),
+])
+def test_fp8_rejects_bad_arguments(lib, kw, status):
+    st = fp8(lib, **kw)
+    assert st == status, (kw, st, iofa.fa_last_error())
+    assert iofa.fa_last_error() != ""
+
+
+def test_fp8_extents_are_one_byte_inputs_and_bf16_output(lib):
+    codes = 2 * 3 * 100 * 128
+    # O (bf16) may start right after Q's codes end, and LSE right after O
+    assert fp8(lib, o=Q + codes + 2 * codes, lse=0) == 1      # LSE still required
+    st = fp8(lib, q=Q, k=Q + codes, v=Q + 2 * codes, o=Q + 3 * codes,
+             lse=Q + 5 * codes, B=0)
+    assert st == 0
+
+
+def test_fp8_empty_problem(lib):
+    assert fp8(lib, q=0, k=0, v=0, o=0, lse=0, N=0) == 0

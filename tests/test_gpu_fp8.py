@@ -1,0 +1,202 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8) against the fp64 oracle
+(standard attention of the decoded, scaled E4M3 inputs), through the C ABI.
+
+Error sources on the GPU side and the bars derived from them:
+
+* Scores: code products are exact; the 64-deep FP8 MFMA accumulates them in
+  fp32 with an internal alignment error measured at up to 2^-12.8 of the sum
+  of the products' magnitudes; the bar allows eps_s = 2^-10 * |scale| * sq *
+  sk * max_j sum_c |q8_ic k8_jc| (log units), plus 2^-20 (1 + |s|) for the
+  fp32 scale and exponential.
+* Weights: p8 = 8 * 2^(s - m) is rounded to E4M3 for the P V product
+  (relative error <= 2^-4 while p8 >= 2^-6; absolute <= 2^-10 below, where
+  the key's weight is under 2^-9 of the row maximum's, hence the
+  normalised weight error is <= 2^-13 since l = sum p8 >= 8).  The row sum
+  uses the unrounded fp32 weights.
+* Output: rounded to bf16 (2^-8 relative).
+
+So |O - O_ref| <= ((1 + 2^-4) e^(2 eps) - 1) * sum_j w_j |v_j|
+                  + 2^-13 * sum_{j: r_j < 2^-8} |v_j| + 2^-8 (|O_ref| + those)
+with r_j = e^(s_j - max s) (2^-8 instead of 2^-9 covers the score error),
+and |LSE - LSE_ref| <= eps + 1e-5 (1 + |LSE_ref|).
+
+Exact-weight inputs make the rounding of P vanish, which gives a tight bar
+that any layout or indexing mistake fails: Q and K codes are small integers
+and scale * sq * sk = ln 2 (fp32), so the kernel's log2-domain scores are
+integers and every p8 is a power of two that E4M3 holds exactly (scores span
+at most 12 per row).  Then O is exact up to the MFMA accumulation (2^-10 of
+sum_j w_j |v_j|) and bf16 rounding (2^-8 |O|), and LSE up to 1e-6 (1 + |LSE|).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_softmax_04_amd as iofa
+import oracle
+from helpers import widen
+from workloads import default_scale, make_qkv_fp8
+
+pytestmark = pytest.mark.gpu
+
+LN2_F32 = float(np.float32(math.log(2.0)))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    iofa.load_library()
+    return torch.device("cuda:0")
+
+
+def _run(q8, k8, v8, scale, sq, sk, sv, dev):
+    o, lse = iofa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), sq, sk, sv, scale=scale)
+    torch.cuda.synchronize()
+    return widen(o.cpu()), lse.cpu().double().numpy()
+
+
+def _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=None):
+    """Per-element and per-row bars of the module docstring (for the rows
+    ``rows`` of every head, or all rows)."""
+    qd, kd, vd = (oracle.decode_e4m3(t.numpy()) for t in (q8, k8, v8))
+    qv, kv, vv = oracle.fp8_values(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv)
+    if rows is not None:
+        qd, qv = qd[:, :, rows], qv[:, :, rows]
+    c = abs(float(np.float32(scale))) * float(np.float32(sq)) * float(np.float32(sk))
+    B, H = qd.shape[:2]
+    bound = np.empty_like(o_ref)
+    eps_all = np.empty(o_ref.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            mag = np.abs(qd[b, h]) @ np.abs(kd[b, h]).T            # sum_c |q8 k8|
+            s = float(np.float32(scale)) * (qv[b, h] @ kv[b, h].T)
+            eps = 2.0 ** -10 * c * mag.max(axis=1) + 2.0 ** -20 * (1 + np.abs(s).max(axis=1))
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            r = w.copy()
+            w /= w.sum(axis=1, keepdims=True)
+            absv = np.abs(vv[b, h])
+            f = (1 + 2.0 ** -4) * np.exp(2 * eps) * (1 + 2.0 ** -20) - 1
+            t1 = f[:, None] * (w @ absv) + 2.0 ** -13 * ((r < 2.0 ** -8) @ absv)
+            bound[b, h] = t1 + 2.0 ** -8 * (np.abs(o_ref[b, h]) + t1) + 1e-30
+            eps_all[b, h] = eps
+    return bound, eps_all
+
+
+def _check_random(q8, k8, v8, scale, sq, sk, sv, dev, label):
+    o, lse = _run(q8, k8, v8, scale, sq, sk, sv, dev)
+    o_ref, lse_ref = oracle.fp8_attention(q8.numpy(), k8.numpy(), v8.numpy(), scale, sq, sk, sv)
+    bound, eps = _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref)
+    err = np.abs(o - o_ref)
+    relf = np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-300)
+    lerr = np.abs(lse - lse_ref)
+    lbar = eps + 1e-5 * (1 + np.abs(lse_ref))
+    print(f"{label}: rel_f={relf:.3e} worst err/bar={np.max(err / bound):.3f} "
+          f"lse worst err/bar={np.max(lerr / lbar):.3f}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), label
+    assert (err <= bound).all(), label
+    assert (lerr <= lbar).all(), label
+
+
+def _exact_weight_inputs(B, H, N, d, seed, nnz=3):
+    """Q and K rows with nnz entries of +-1 (so scores lie in [-nnz, nnz]),
+    V codes from N(0, 1) scaled to E4M3's range; returns codes and sv."""
+    g = torch.Generator().manual_seed(seed)
+
+    def sparse_pm1():
+        x = torch.zeros((B, H, N, d))
+        idx = torch.rand((B, H, N, d), generator=g).argsort(dim=-1)[..., :nnz]
+        sgn = torch.randint(0, 2, (B, H, N, nnz), generator=g).float() * 2 - 1
+        x.scatter_(-1, idx, sgn)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+
+    q8, k8 = sparse_pm1(), sparse_pm1()
+    v = torch.randn((B, H, N, d), generator=g)
+    sv = float(np.float32(float(v.abs().max()) / 448.0))
+    v8 = (v / sv).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    return q8, k8, v8, sv
+
+
+def _check_exact(q8, k8, v8, scale, sv, dev, label):
+    o, lse = _run(q8, k8, v8, scale, 1.0, 1.0, sv, dev)
+    o_ref, lse_ref = oracle.fp8_attention(q8.numpy(), k8.numpy(), v8.numpy(), scale, 1.0, 1.0, sv)
+    absref, _ = oracle.fp8_attention(q8.numpy(), k8.numpy(), v8.numpy() & 0x7F, scale,
+                                     1.0, 1.0, sv)                  # sum_j w_j |v_j|
+    bar = 2.0 ** -10 * absref + 2.0 ** -8 * np.abs(o_ref) + 1e-30
+    err = np.abs(o - o_ref)
+    lerr = np.abs(lse - lse_ref)
+    print(f"{label}: worst err/bar={np.max(err / bar):.3f} "
+          f"max lse err={lerr.max():.2e}", flush=True)
+    assert (err <= bar).all(), label
+    assert (lerr <= 1e-6 * (1 + np.abs(lse_ref))).all(), label
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_exact_weights_match_oracle(d, dev):
+    for N in (1, 7, 63, 64, 65, 128, 129, 300, 1000):
+        q8, k8, v8, sv = _exact_weight_inputs(1, 2, N, d, seed=N * 7 + d)
+        _check_exact(q8, k8, v8, LN2_F32, sv, dev, f"exact d={d} N={N}")
+
+
+def test_fp8_exact_weights_negative_scale_and_heads(dev):
+    q8, k8, v8, sv = _exact_weight_inputs(2, 3, 333, 128, seed=5)
+    _check_exact(q8, k8, v8, -LN2_F32, sv, dev, "exact negative scale B2 H3 N333")
+
+
+def test_fp8_reference_moves_every_tile(dev):
+    # one query direction, key tile t scores t (t = 0..9): every tile's
+    # maximum exceeds the reference, p8 reaches 16 per key, so a lane's sum
+    # over its 32 keys passes 448 and the tile is redone against its maximum
+    N, d = 640, 128
+    q = torch.zeros((1, 1, N, d))
+    q[..., 0] = 1.0
+    k = torch.zeros((1, 1, N, d))
+    k[0, 0, :, 0] = torch.arange(N).div(64, rounding_mode="floor").float()
+    q8 = q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    g = torch.Generator().manual_seed(17)
+    v8 = (torch.randn((1, 1, N, d), generator=g) * 64).to(torch.float8_e4m3fn)
+    v8 = v8.view(torch.uint8).contiguous()
+    _check_exact(q8, k8, v8, LN2_F32, 0.01, dev, "reference moves every tile")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_random_inputs_within_derived_bound(d, dev):
+    for N in (1, 33, 100, 257, 1000):
+        (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(1, 2, N, d, seed_base=N + d)
+        _check_random(q8, k8, v8, default_scale(d), sq, sk, sv, dev, f"random d={d} N={N}")
+
+
+def test_fp8_stress_distribution(dev):
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(1, 2, 700, 128, seed_base=3, dist="stress")
+    _check_random(q8, k8, v8, default_scale(128), sq, sk, sv, dev, "stress N=700")
+
+
+def test_fp8_full_size_sampled_rows(dev):
+    # the benchmarked launch: B2 H16 N4096 d128, checked on sampled rows
+    B, H, N, d = 2, 16, 4096, 128
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(B, H, N, d, seed_base=3000)
+    scale = default_scale(d)
+    o, lse = _run(q8, k8, v8, scale, sq, sk, sv, dev)
+    rows = np.array([0, 1, 127, 128, 2047, 3001, 4094, 4095])
+    o_ref, lse_ref = oracle.fp8_attention_rows(q8.numpy(), k8.numpy(), v8.numpy(), scale,
+                                               sq, sk, sv, rows)
+    bound, eps = _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=rows)
+    err = np.abs(o[:, :, rows] - o_ref)
+    relf = np.linalg.norm(o[:, :, rows] - o_ref) / np.linalg.norm(o_ref)
+    print(f"full size sampled rows: rel_f={relf:.3e} worst err/bar={np.max(err / bound):.3f}",
+          flush=True)
+    assert (err <= bound).all()
+    assert (np.abs(lse[:, :, rows] - lse_ref) <= eps + 1e-5 * (1 + np.abs(lse_ref))).all()
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+def test_fp8_is_deterministic(dev):
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(1, 4, 900, 128, seed_base=11)
+    a = iofa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), sq, sk, sv)
+    b = iofa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), sq, sk, sv)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])

@@ -617,3 +617,117 @@ def test_planted_backward_mistakes_fail_a_pin(kind):
     else:
         dq = 0.5 * (p * (dp - D[:, None])).T @ k[0, 0]
     assert np.abs(dq - good[0][0, 0]).max() > 1e-6
+
+
+# ------------------------------------------------------------- FP8 inputs
+
+def test_decode_e4m3_every_code():
+    # library conversion of all 256 codes (torch's float8_e4m3fn)
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def test_decode_e4m3_format_landmarks():
+    # values fixed by the format: bias 7, 3 mantissa bits, no infinities
+    d = lambda c: float(oracle.decode_e4m3(np.array([c], dtype=np.uint8))[0])  # noqa: E731
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0          # largest finite
+    assert d(0x08) == 2.0 ** -6                             # smallest normal
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9  # subnormals
+    assert d(0x38) == 1.0 and d(0x3C) == 1.5 and d(0x40) == 2.0
+    assert d(0x00) == 0.0 and d(0x80) == 0.0 and np.signbit(d(0x80))
+    pos = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    assert (np.diff(pos) > 0).all()
+    # spacing within binade e (codes 8e .. 8e+7, e >= 1) is 2^(e - 10)
+    for e in range(1, 16):
+        hi = min(8 * e + 8, 0x7F)
+        assert (np.diff(pos[8 * e:hi]) == 2.0 ** (e - 10)).all()
+
+
+def _fp8_tiny(seed, B=1, H=2, N=9, d=4):
+    rng = np.random.default_rng(seed)
+    codes = [rng.integers(0, 256, size=(B, H, N, d)).astype(np.uint8) for _ in range(3)]
+    for c in codes:
+        c[(c & 0x7F) == 0x7F] = 0x3A        # finite codes only
+    return codes
+
+
+def test_fp8_attention_against_brute_force():
+    # plain Python loops over values decoded by torch's conversion
+    q8, k8, v8 = _fp8_tiny(3)
+    scale, sq, sk, sv = 0.375, 0.0625, 0.5, 3.0
+    o, lse = oracle.fp8_attention(q8, k8, v8, scale, sq, sk, sv)
+    dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).double().numpy()  # noqa: E731
+    q, k, v = sq * dec(q8), sk * dec(k8), sv * dec(v8)
+    B, H, N, d = q.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                s = [scale * sum(q[b, h, i, c] * k[b, h, j, c] for c in range(d))
+                     for j in range(N)]
+                m = max(s)
+                f = [math.exp(x - m) for x in s]
+                l_ = sum(f)
+                for c in range(d):
+                    ref = sum(f[j] * v[b, h, j, c] for j in range(N)) / l_
+                    assert abs(o[b, h, i, c] - ref) <= 1e-12 * (1 + abs(ref))
+                assert abs(lse[b, h, i] - (m + math.log(l_))) <= 1e-12 * (1 + abs(m))
+
+
+def test_fp8_attention_closed_forms_and_scale_roles():
+    q8, k8, v8 = _fp8_tiny(4, N=11, d=8)
+    # every key row equal: uniform weights, O = v_scale * mean of the V values,
+    # LSE = the common score + ln N
+    k_eq = np.broadcast_to(k8[:, :, :1], k8.shape).copy()
+    sq, sk, sv, scale = 0.25, 2.0, 0.125, 0.5
+    o, lse = oracle.fp8_attention(q8, k_eq, v8, scale, sq, sk, sv)
+    vals = oracle.decode_e4m3(v8) * sv
+    assert np.abs(o - vals.mean(axis=2, keepdims=True)).max() <= 1e-12 * np.abs(vals).max()
+    s0 = scale * sq * sk * (oracle.decode_e4m3(q8) * oracle.decode_e4m3(k_eq[:, :, :1])).sum(-1)
+    assert np.abs(lse - (s0 + math.log(11))).max() <= 1e-12 * (1 + np.abs(s0).max())
+    # only scale * q_scale * k_scale enters the scores; O is linear in v_scale
+    o1, l1 = oracle.fp8_attention(q8, k8, v8, 0.5, 0.25, 2.0, 1.0)
+    o2, l2 = oracle.fp8_attention(q8, k8, v8, 0.125, 4.0, 0.5, 3.0)
+    assert np.abs(o2 - 3.0 * o1).max() <= 1e-12 * (1 + np.abs(o1).max())
+    assert np.abs(l2 - l1).max() <= 1e-12 * (1 + np.abs(l1).max())
+
+
+@pytest.mark.parametrize("kind", ["bias8", "subnormal_exp", "mantissa16", "no_sign",
+                                  "v_scale_on_q"])
+def test_planted_fp8_mistakes_fail_a_pin(kind, monkeypatch):
+    import oracle.fp8 as of
+    real = of.decode_e4m3
+
+    def mutant_decode(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign, e, m = (c >> 7) & 1, (c >> 3) & 15, (c & 7).astype(np.float64)
+        bias = 8 if kind == "bias8" else 7
+        div = 16.0 if kind == "mantissa16" else 8.0
+        sub_e = -7 if kind == "subnormal_exp" else -6
+        mag = np.where(e == 0, np.ldexp(m / div, sub_e),
+                       np.ldexp(1.0 + m / div, (e - bias).astype(np.int32)))
+        mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+        return mag if kind == "no_sign" else np.where(sign == 1, -mag, mag)
+
+    if kind == "v_scale_on_q":
+        def mutant_values(q8, k8, v8, q_scale, k_scale, v_scale):
+            return (v_scale * real(q8), k_scale * real(k8), q_scale * real(v8))
+        monkeypatch.setattr(of, "fp8_values", mutant_values)
+    else:
+        monkeypatch.setattr(of, "decode_e4m3", mutant_decode)
+        monkeypatch.setattr(oracle, "decode_e4m3", mutant_decode)
+    pins = (test_decode_e4m3_every_code, test_decode_e4m3_format_landmarks,
+            test_fp8_attention_against_brute_force,
+            test_fp8_attention_closed_forms_and_scale_roles)
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"mutant {kind!r} passed every pin"

@@ -64,6 +64,26 @@ def make_qkv(B, H, N, d, dtype="bf16", seed_base=0, dist="normal"):
     return tuple(out)
 
 
+E4M3_MAX = 448.0
+
+
+def make_qkv_fp8(B, H, N, d, seed_base=0, dist="normal"):
+    """FP8 (OCP E4M3) inputs with one scale per tensor: the fp32 tensors of
+    ``make_qkv(..., "fp32", ...)``, each divided by its scale
+    amax / 448 (fp32) and rounded to E4M3 by torch's float8_e4m3fn
+    conversion (nearest-even), so the largest magnitude maps to 448.
+    Returns (q8, k8, v8) as CPU uint8 code tensors and the three fp32
+    scales (q_scale, k_scale, v_scale)."""
+    codes, scales = [], []
+    for t in make_qkv(B, H, N, d, "fp32", seed_base, dist):
+        amax = float(t.abs().max()) if t.numel() else 0.0
+        s = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+        c = (t / s).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        codes.append(c.view(torch.uint8).contiguous())
+        scales.append(s)
+    return tuple(codes), tuple(scales)
+
+
 def workload_qkv(index):
     """Inputs of named workload ``index`` (1..5): (q, k, v, scale, spec)."""
     spec = WORKLOADS[index]
