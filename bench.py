@@ -28,7 +28,8 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 FLOP/
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 FUSED_KERNEL_SOURCES = ["io_aware_softmax_04_amd/csrc/fa_fwd_gfx950.hip",
-                        "io_aware_softmax_04_amd/csrc/fa_device.h"]
+                        "io_aware_softmax_04_amd/csrc/fa_device.h",
+                        "io_aware_softmax_04_amd/csrc/fa_sched.h"]
 TRAFFIC_FILE = "profiles/traffic_fused_fwd_{tag}.md"
 FUSED_KERNEL_NAME = "fa_fwd_16_kernel"
 COPY_KERNEL_NAME = "__amd_rocclr_copyBuffer"
