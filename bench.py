@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-softmax", action="store_true", help="skip the row-softmax measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the sustained-MFMA ceiling measurement")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
@@ -521,6 +523,21 @@ def fp8_measure(spec, args, torch, iofa, dev):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
 
 
+def mfma_ceiling():
+    """Run the standalone MFMA-ceiling program (a child process) and return
+    its cases: the sustained bf16 and fp8 MFMA rates of the whole chip at the
+    fused kernels' occupancy, with the shader clock they ran at."""
+    import subprocess
+    exe = os.path.join(ROOT, "io_aware_softmax_04_amd", "_lib", "mfma_ceiling")
+    if not os.path.exists(exe):
+        return None
+    proc = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                          timeout=120)
+    if proc.returncode != 0:
+        raise RuntimeError(f"mfma_ceiling failed: {proc.stderr.strip()}")
+    return [json.loads(ln) for ln in proc.stdout.splitlines() if ln.startswith("{")]
+
+
 def softmax_measure(args, torch, iofa, dev):
     """The standalone row softmax on bf16 rows that fit one workgroup (x read
     once, y written once) and on long rows (x read twice).  Roofline: HBM;
@@ -678,6 +695,16 @@ def main():
     if not args.no_softmax:
         line["softmax_rows"] = softmax_measure(args, torch, iofa, dev)
         print(f"[bench] row softmax: {line['softmax_rows']}", file=sys.stderr, flush=True)
+
+    if not args.no_ceiling:
+        cases = mfma_ceiling()
+        if cases:
+            rnd = [c for c in cases if c["case"].startswith("bf16") and "random" in c["case"]]
+            line["mfma_ceiling"] = {"cases": cases}
+            if rnd:
+                line["mfma_ceiling"]["fused_frac_of_bf16_random_ceiling"] = round(
+                    achieved / rnd[0]["tflops"], 4)
+            print(f"[bench] MFMA ceiling: {line['mfma_ceiling']}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -3,7 +3,8 @@
     python -m io_aware_softmax_04_amd.build
 
 Compiles every HIP source for gfx950 with hipcc and links one shared
-library at io_aware_softmax_04_amd/_lib/libiofa.so.  Packed fp32 vector
+library at io_aware_softmax_04_amd/_lib/libiofa.so, plus the standalone
+MFMA-ceiling measurement program _lib/mfma_ceiling.  Packed fp32 vector
 instructions are disabled for all device code.
 """
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libiofa.so")
+CEILING = os.path.join(OUT_DIR, "mfma_ceiling")
+CEILING_SOURCE = "mfma_ceiling.hip"
 
 SOURCES = ["fa_api.cpp", "fa_fwd_gfx950.hip", "fa_naive_gfx950.hip", "fa_merge_gfx950.hip",
            "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip", "fa_fwd_fp8_gfx950.hip"]
@@ -73,6 +76,14 @@ def build(verbose=False, extra_flags=()):
     if rc != 0:
         raise RuntimeError(f"linking libiofa.so failed:\n{out}")
     os.replace(tmp, LIB)
+    tmp = CEILING + ".tmp"
+    cmd = [cc, "-std=c++17", "-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", *extra_flags, os.path.join(CSRC, CEILING_SOURCE),
+           "-o", tmp]
+    rc, out = _run(cmd)
+    if rc != 0:
+        raise RuntimeError(f"building mfma_ceiling failed:\n{out}")
+    os.replace(tmp, CEILING)
     return LIB
 
 
