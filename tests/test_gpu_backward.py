@@ -95,3 +95,21 @@ def test_backward_is_deterministic(dev):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_no_writes_outside_gradients(dev):
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = (t.to(dev) for t in make_qkv(B, H, N, d, "bf16", seed_base=8))
+    do = torch.randn_like(q)
+    o, lse = iofa.forward(q, k, v)
+    guard, n = 4096, B * H * N * d
+    bufs = [torch.full((guard + n + guard,), float("nan"), dtype=torch.bfloat16, device=dev)
+            for _ in range(3)]
+    dq, dk, dv = (b[guard:guard + n].view(B, H, N, d) for b in bufs)
+    ws = torch.empty(iofa.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+    iofa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, iofa.default_scale(d))
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert torch.isnan(b[:guard]).all() and torch.isnan(b[-guard:]).all()
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g).all()

@@ -200,3 +200,36 @@ def test_fp8_is_deterministic(dev):
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("N,d", [(8191, 128), (129, 64), (1, 128)])
+def test_fp8_no_writes_outside_outputs(N, d, dev):
+    B, H = 1, 2
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(B, H, N, d, seed_base=N + 1)
+    guard = 4096
+    n_o = B * H * N * d
+    obuf = torch.full((guard + n_o + guard,), float("nan"), dtype=torch.bfloat16, device=dev)
+    lbuf = torch.full((guard + B * H * N + guard,), -7.0, dtype=torch.float32, device=dev)
+    o = obuf[guard:guard + n_o].view(B, H, N, d)
+    lse = lbuf[guard:guard + B * H * N].view(B, H, N)
+    iofa.fa_fwd_fp8(q8.to(dev), k8.to(dev), v8.to(dev), o, lse, default_scale(d), sq, sk, sv)
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[:guard]).all() and torch.isnan(obuf[-guard:]).all()
+    assert (lbuf[:guard] == -7.0).all() and (lbuf[-guard:] == -7.0).all()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_fp8_float8_tensors_and_side_stream(dev):
+    # float8_e4m3fn tensors are accepted as codes; work goes to the caller's stream
+    (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(1, 2, 300, 128, seed_base=21)
+    qf, kf, vf = (t.view(torch.float8_e4m3fn).to(dev) for t in (q8, k8, v8))
+    s = torch.cuda.Stream(device=dev)
+    o = torch.empty((1, 2, 300, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, 2, 300), dtype=torch.float32, device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        iofa.fa_fwd_fp8(qf, kf, vf, o, lse, default_scale(128), sq, sk, sv, stream=s)
+    s.synchronize()
+    ref_o, ref_l = _run(q8, k8, v8, default_scale(128), sq, sk, sv, dev)
+    assert np.array_equal(widen(o.cpu()), ref_o)
+    assert np.array_equal(lse.cpu().double().numpy(), ref_l)
