@@ -18,8 +18,12 @@
 //
 // Workgroup = 256 threads; a thread holds EPT elements loaded as 16-byte
 // vectors when a row's length keeps rows 16-byte aligned (VEC elements per
-// load), else one element per load.  Arithmetic is fp32 with the accurate
-// expf / logf (the kernels are bandwidth-bound).
+// load), else one element per load.  Arithmetic is fp32.  fp32 outputs use
+// the accurate expf; 16-bit outputs use the hardware exp2 (see exp_nonpos),
+// whose relative error (below 2e-5 while the result is above bf16's
+// smallest subnormal) is far under the output's own rounding and which costs
+// three instructions instead of about twelve, so the kernels stay bound by
+// memory rather than by the vector unit.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -74,6 +78,25 @@ struct Elem {
     *reinterpret_cast<u32x4*>(static_cast<char*>(p) + i * BYTES) = w;
   }
 };
+
+// 2^bias * e^t for t <= 0 (t = x - m): the accurate expf (bias 0) for fp32
+// outputs, the hardware exp2 of t log2 e + 64 for 16-bit ones.  v_exp_f32
+// flushes subnormal results; the bias keeps every result above e^-133 (the
+// smallest bf16 subnormal is 2^-133) in fp32's normal range.  The same factor
+// scales every l, so the block merge and y = (2^bias e^t) / l are unchanged
+// and only the log-sum-exp subtracts it (row sums stay below 2^95).
+template <int KIND>
+constexpr float kExpBias = KIND == 0 ? 0.f : 64.f;
+template <int KIND>
+__device__ inline float exp_nonpos(float t) {
+  if constexpr (KIND == 0) return expf(t);
+  return __builtin_amdgcn_exp2f(fmaf(t, kLog2e, kExpBias<KIND>));
+}
+// ln l - bias ln 2: the log-sum-exp's share of the row sum.
+template <int KIND>
+__device__ inline float log_sum(float l) {
+  return logf(l) - kExpBias<KIND> * kLn2;
+}
 
 // Block merge of two (m, l) pairs; -inf maxima (no values yet) merge as the
 // identity.
@@ -151,7 +174,7 @@ __device__ inline void store_chunk(void* row, int64_t n, int64_t c0, const float
 }
 
 // (m, l) of the values in v (some may be -inf).
-template <int EPT>
+template <int KIND, int EPT>
 __device__ inline float2 chunk_stats(const float* v, float* red) {
   float m = -__builtin_inff();
 #pragma unroll
@@ -160,7 +183,7 @@ __device__ inline float2 chunk_stats(const float* v, float* red) {
   if (m == -__builtin_inff()) return make_float2(m, 0.f);
   float l = 0.f;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) l += expf(v[i] - m);
+  for (int i = 0; i < EPT; ++i) l += exp_nonpos<KIND>(v[i] - m);
   l = block_reduce(wave_sum(l), red, [](float a, float b) { return a + b; });
   return make_float2(m, l);
 }
@@ -178,12 +201,12 @@ __global__ __launch_bounds__(kThreads) void softmax_short_kernel(const void* __r
   char* yr = static_cast<char*>(Y) + r * n * E::BYTES;
   float v[E::EPT];
   load_chunk<KIND, VECTOR>(xr, n, 0, v);
-  const float2 ml = chunk_stats<E::EPT>(v, red);
+  const float2 ml = chunk_stats<KIND, E::EPT>(v, red);
   const float inv = 1.f / ml.y;
 #pragma unroll
-  for (int i = 0; i < E::EPT; ++i) v[i] = expf(v[i] - ml.x) * inv;
+  for (int i = 0; i < E::EPT; ++i) v[i] = exp_nonpos<KIND>(v[i] - ml.x) * inv;
   store_chunk<KIND, VECTOR>(yr, n, 0, v);
-  if (LSE && threadIdx.x == 0) LSE[r] = ml.x + logf(ml.y);
+  if (LSE && threadIdx.x == 0) LSE[r] = ml.x + log_sum<KIND>(ml.y);
 }
 
 // Long rows, pass 1: (m, l) of chunk c of row r (workgroup r * chunks + c).
@@ -197,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const void* __r
   const char* xr = static_cast<const char*>(X) + r * n * E::BYTES;
   float v[E::EPT];
   load_chunk<KIND, VECTOR>(xr, n, c * E::CHUNK, v);
-  const float2 ml = chunk_stats<E::EPT>(v, red);
+  const float2 ml = chunk_stats<KIND, E::EPT>(v, red);
   if (threadIdx.x == 0) stats[r * chunks + c] = ml;
 }
 
@@ -221,9 +244,9 @@ __global__ __launch_bounds__(kThreads) void softmax_normalize_kernel(
   load_chunk<KIND, VECTOR>(xr, n, c * E::CHUNK, v);
   const float inv = 1.f / ml.y;
 #pragma unroll
-  for (int i = 0; i < E::EPT; ++i) v[i] = expf(v[i] - ml.x) * inv;
+  for (int i = 0; i < E::EPT; ++i) v[i] = exp_nonpos<KIND>(v[i] - ml.x) * inv;
   store_chunk<KIND, VECTOR>(yr, n, c * E::CHUNK, v);
-  if (LSE && c == 0 && threadIdx.x == 0) LSE[r] = ml.x + logf(ml.y);
+  if (LSE && c == 0 && threadIdx.x == 0) LSE[r] = ml.x + log_sum<KIND>(ml.y);
 }
 
 template <int KIND, bool VECTOR>
