@@ -39,8 +39,11 @@ NAIVE_KERNEL_NAMES = ["naive_scores_16", "naive_softmax_16", "naive_pv_16"]
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # the GPU's clock and power state settle within a few hundred
+    # milliseconds of sustained load (the first ~30 ms run about 12% slower),
+    # so the default warm-up covers about 0.6 s before the timed steps
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--no-naive", action="store_true", help="skip the naive contrast")
     p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
@@ -248,7 +251,7 @@ def summarise_trace(trace_dir, index, spec, bench_args):
         "```",
         f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run --output-format csv -- "
         f"python bench.py {bench_args}",
-        f"python bench.py --workload {index} --trace-from {trace_dir} --trace-cmd '{bench_args}'",
+        f"python bench.py --workload {index} --trace-from {trace_dir} --trace-cmd='{bench_args}'",
         "```",
         "",
         f"One row per kernel and launch grid (work-items); the fused forward at this "
@@ -278,6 +281,9 @@ def summarise_trace(trace_dir, index, spec, bench_args):
 SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES"]
 SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
+# the counter pass times the fused kernel only, after the default warm-up
+SQ_BENCH_ARGS = ("--steps 20 --no-naive --no-splitkv --no-softmax --no-backward --no-fp8 "
+                 "--no-ceiling --no-cpu-baseline")
 SIMDS = 1024                 # 256 CUs x 4
 
 
@@ -323,7 +329,7 @@ def summarise_sq(pmc_dir, index, spec):
         "",
         "```",
         f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {pmc_dir} -o run --output-format csv -- "
-        f"python bench.py --workload {index} --steps 3 --warmup 1 --no-naive --no-cpu-baseline",
+        f"python bench.py --workload {index} {SQ_BENCH_ARGS}",
         f"python bench.py --workload {index} --sq-from {pmc_dir}",
         "```",
         "",
@@ -370,12 +376,19 @@ def read_traffic(spec):
     return int(fields["bytes_per_launch"])
 
 
-def time_launches(fn, steps, warmup, torch):
-    """Run ``fn`` warmup + steps times; returns (wall ms per step, mean launch
-    ms from HIP events recorded on the launch stream around each call)."""
+def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
+    """Run ``fn`` warmup times (then keep running it until ``warm_seconds``
+    have passed, so the GPU's clock has settled under load), then steps
+    times; returns (wall ms per step, mean launch ms from HIP events recorded
+    on the launch stream around each call)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
@@ -454,9 +467,10 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
                      dtype=torch.uint8, device=dev)
     flops = 4.0 * B * H * N * N * d
     steps = max(5, min(args.steps, 30))
-    _, f_ms = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch)
+    _, f_ms = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch,
+                            warm_seconds=0.3)
     _, s_ms = time_launches(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g),
-                            steps, 3, torch)
+                            steps, 3, torch, warm_seconds=0.3)
     rows = B * H * N
     flat = ws.view(torch.float32)
     o_part = flat[:g * rows * d].view(g, rows, d)
@@ -464,7 +478,7 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     o2 = torch.empty((rows, d), dtype=q.dtype, device=dev)
     l2 = torch.empty((rows,), dtype=torch.float32, device=dev)
     _, m_ms = time_launches(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2),
-                            steps, 3, torch)
+                            steps, 3, torch, warm_seconds=0.3)
     merge_bytes = g * rows * (d + 1) * 4 + rows * (d * q.element_size() + 4)
     return {
         "workload": f"{spec['dtype']} B{B} H{H} N{N} d{d} (one GPU's share of an 8-way head split)",
@@ -494,7 +508,7 @@ def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
     ws = torch.empty(iofa.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
     steps = max(5, min(args.steps, 30))
     _, ms = time_launches(lambda: iofa.fa_bwd(qd, kd, vd, o, do, lse, dq, dk, dv, ws, scale),
-                          steps, 3, torch)
+                          steps, 3, torch, warm_seconds=0.3)
     alg = 10.0 * B * H * N * N * d
     return {"workload": spec["name"], "ms": round(ms, 4),
             "tflops_algorithmic": round(alg / (ms * 1e-3) / 1e12, 1),
@@ -515,7 +529,7 @@ def fp8_measure(spec, args, torch, iofa, dev):
     scale = default_scale(d)
     steps = max(5, min(args.steps, 50))
     _, ms = time_launches(lambda: iofa.fa_fwd_fp8(q8, k8, v8, o, lse, scale, sq, sk, sv),
-                          steps, min(args.warmup, 5), torch)
+                          steps, min(args.warmup, 5), torch, warm_seconds=0.3)
     tf = 4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12
     return {"workload": f"fp8 (E4M3, per-tensor scales) B{B} H{H} N{N} d{d}, bf16 output",
             "ms": round(ms, 4), "tflops": round(tf, 1),
@@ -553,7 +567,7 @@ def softmax_measure(args, torch, iofa, dev):
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         steps = max(5, min(args.steps, 30))
         _, ms = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
-                              steps, 3, torch)
+                              steps, 3, torch, warm_seconds=0.3)
         alg = rows * n * 2 * 2 + rows * 4
         reads = 1 if nb == 0 else 2
         moved = rows * n * 2 * (reads + 1) + rows * 4
@@ -669,7 +683,8 @@ def main():
                 iofa.fa_naive_fwd(qd, kd, vd, o2, lse2, s_ws, p_ws, scale)
 
             nsteps = max(3, min(args.steps, 20))
-            n_wall, n_ev = time_launches(naive, nsteps, min(args.warmup, 3), torch)
+            n_wall, n_ev = time_launches(naive, nsteps, min(args.warmup, 3), torch,
+                                         warm_seconds=0.3)
             line["naive_contrast"] = {
                 "ms_per_call": round(n_ev, 4),
                 "tflops_equiv": round(flops / (n_ev * 1e-3) / 1e12, 2),
