@@ -4,8 +4,9 @@ tolerances, and comparisons."""
 import numpy as np
 import torch
 
+import io_aware_softmax_04_amd as iofa
 import oracle
-from workloads import raw_bits
+from workloads import default_scale, make_qkv, raw_bits
 
 # Parity bars.  16-bit inputs: max-abs 1e-2 and relative Frobenius 5e-3 on O
 # (oracle fed the same rounded inputs); fp32 inputs: 1e-5 for both.  LSE:
@@ -82,3 +83,70 @@ def sample_rows(N, seed=0, edge=64, middle=64):
     rows = set(range(min(edge, N))) | set(range(max(0, N - edge), N))
     rows |= set(rng.integers(0, N, size=middle).tolist())
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def fp8_output_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=None):
+    """Per-element bar on O and per-row score-error bound eps of the FP8
+    forward (derivation in tests/test_gpu_fp8.py's docstring), for the rows
+    ``rows`` of every head, or all rows.  q8, k8, v8: CPU uint8 code
+    tensors; o_ref: the oracle's output for those rows."""
+    qd, kd, vd = (oracle.decode_e4m3(t.numpy()) for t in (q8, k8, v8))
+    qv, kv, vv = oracle.fp8_values(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv)
+    if rows is not None:
+        qd, qv = qd[:, :, rows], qv[:, :, rows]
+    c = abs(float(np.float32(scale))) * float(np.float32(sq)) * float(np.float32(sk))
+    B, H = qd.shape[:2]
+    bound = np.empty_like(o_ref)
+    eps_all = np.empty(o_ref.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            mag = np.abs(qd[b, h]) @ np.abs(kd[b, h]).T            # sum_c |q8 k8|
+            s = float(np.float32(scale)) * (qv[b, h] @ kv[b, h].T)
+            eps = 2.0 ** -10 * c * mag.max(axis=1) + 2.0 ** -20 * (1 + np.abs(s).max(axis=1))
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            r = w.copy()
+            w /= w.sum(axis=1, keepdims=True)
+            absv = np.abs(vv[b, h])
+            f = (1 + 2.0 ** -4) * np.exp(2 * eps) * (1 + 2.0 ** -20) - 1
+            t1 = f[:, None] * (w @ absv) + 2.0 ** -13 * ((r < 2.0 ** -8) @ absv)
+            bound[b, h] = t1 + 2.0 ** -8 * (np.abs(o_ref[b, h]) + t1) + 1e-30
+            eps_all[b, h] = eps
+    return bound, eps_all
+
+
+def check_backward(B, H, N, d, dtype, seed, dev, dist="normal", label=""):
+    """Run the fused forward and fa_bwd on seeded inputs and hold dQ, dK, dV
+    to the bars of tests/test_gpu_backward.py's docstring against the fp64
+    gradient oracle.  Returns {name: (rel_f, max_abs / max|ref|)}."""
+    q, k, v = make_qkv(B, H, N, d, dtype, seed_base=seed, dist=dist)
+    g = torch.Generator().manual_seed(seed + 7)
+    do = torch.randn((B, H, N, d), generator=g).to(q.dtype)
+    scale = default_scale(d)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = iofa.forward(qd, kd, vd, scale)
+    dq, dk, dv = iofa.backward(qd, kd, vd, o, lse, dod, scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(widen(q), widen(k), widen(v), widen(do),
+                                    float(np.float32(scale)))
+    u = UNIT_ROUNDOFF[q.dtype]
+    out = {}
+    qw, kw, vw, dw = widen(q), widen(k), widen(v), widen(do)
+    sum_err = 4 * d * 2.0 ** -24 * np.abs(dw).max() * np.abs(vw).max()
+    zero_bound = {"dq": sum_err * scale * np.abs(kw).max(),
+                  "dk": sum_err * scale * np.abs(qw).max(), "dv": 0.0}
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        gw = widen(got.cpu())
+        assert np.isfinite(gw).all(), name
+        if np.abs(r).max() == 0:
+            print(f"{label} {name}: exact zero, max|got|={np.abs(gw).max():.3e} "
+                  f"(<= {zero_bound[name]:.2e})", flush=True)
+            assert np.abs(gw).max() <= zero_bound[name], (label, name)
+            continue
+        relf = np.linalg.norm(gw - r) / np.linalg.norm(r)
+        rmax = np.abs(gw - r).max() / np.abs(r).max()
+        out[name] = (relf, rmax)
+        print(f"{label} {name}: rel_f={relf:.3e} (<= {3 * u:.2e}) "
+              f"max_abs/max|ref|={rmax:.3e} (<= {12 * u:.2e})", flush=True)
+        assert relf <= 3 * u, (label, name, relf)
+        assert rmax <= 12 * u, (label, name, rmax)
+    return out

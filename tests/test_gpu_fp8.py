@@ -36,7 +36,7 @@ import torch
 
 import io_aware_softmax_04_amd as iofa
 import oracle
-from helpers import widen
+from helpers import fp8_output_bound, widen
 from workloads import default_scale, make_qkv_fp8
 
 pytestmark = pytest.mark.gpu
@@ -58,37 +58,10 @@ def _run(q8, k8, v8, scale, sq, sk, sv, dev):
     return widen(o.cpu()), lse.cpu().double().numpy()
 
 
-def _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=None):
-    """Per-element and per-row bars of the module docstring (for the rows
-    ``rows`` of every head, or all rows)."""
-    qd, kd, vd = (oracle.decode_e4m3(t.numpy()) for t in (q8, k8, v8))
-    qv, kv, vv = oracle.fp8_values(q8.numpy(), k8.numpy(), v8.numpy(), sq, sk, sv)
-    if rows is not None:
-        qd, qv = qd[:, :, rows], qv[:, :, rows]
-    c = abs(float(np.float32(scale))) * float(np.float32(sq)) * float(np.float32(sk))
-    B, H = qd.shape[:2]
-    bound = np.empty_like(o_ref)
-    eps_all = np.empty(o_ref.shape[:3])
-    for b in range(B):
-        for h in range(H):
-            mag = np.abs(qd[b, h]) @ np.abs(kd[b, h]).T            # sum_c |q8 k8|
-            s = float(np.float32(scale)) * (qv[b, h] @ kv[b, h].T)
-            eps = 2.0 ** -10 * c * mag.max(axis=1) + 2.0 ** -20 * (1 + np.abs(s).max(axis=1))
-            w = np.exp(s - s.max(axis=1, keepdims=True))
-            r = w.copy()
-            w /= w.sum(axis=1, keepdims=True)
-            absv = np.abs(vv[b, h])
-            f = (1 + 2.0 ** -4) * np.exp(2 * eps) * (1 + 2.0 ** -20) - 1
-            t1 = f[:, None] * (w @ absv) + 2.0 ** -13 * ((r < 2.0 ** -8) @ absv)
-            bound[b, h] = t1 + 2.0 ** -8 * (np.abs(o_ref[b, h]) + t1) + 1e-30
-            eps_all[b, h] = eps
-    return bound, eps_all
-
-
 def _check_random(q8, k8, v8, scale, sq, sk, sv, dev, label):
     o, lse = _run(q8, k8, v8, scale, sq, sk, sv, dev)
     o_ref, lse_ref = oracle.fp8_attention(q8.numpy(), k8.numpy(), v8.numpy(), scale, sq, sk, sv)
-    bound, eps = _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref)
+    bound, eps = fp8_output_bound(q8, k8, v8, scale, sq, sk, sv, o_ref)
     err = np.abs(o - o_ref)
     relf = np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-300)
     lerr = np.abs(lse - lse_ref)
@@ -163,7 +136,7 @@ def test_fp8_reference_moves_every_tile(dev):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_fp8_random_inputs_within_derived_bound(d, dev):
+def test_fp8_random_inputs_withinfp8_output_bound(d, dev):
     for N in (1, 33, 100, 257, 1000):
         (q8, k8, v8), (sq, sk, sv) = make_qkv_fp8(1, 2, N, d, seed_base=N + d)
         _check_random(q8, k8, v8, default_scale(d), sq, sk, sv, dev, f"random d={d} N={N}")
@@ -183,7 +156,7 @@ def test_fp8_full_size_sampled_rows(dev):
     rows = np.array([0, 1, 127, 128, 2047, 3001, 4094, 4095])
     o_ref, lse_ref = oracle.fp8_attention_rows(q8.numpy(), k8.numpy(), v8.numpy(), scale,
                                                sq, sk, sv, rows)
-    bound, eps = _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=rows)
+    bound, eps = fp8_output_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=rows)
     err = np.abs(o[:, :, rows] - o_ref)
     relf = np.linalg.norm(o[:, :, rows] - o_ref) / np.linalg.norm(o_ref)
     print(f"full size sampled rows: rel_f={relf:.3e} worst err/bar={np.max(err / bound):.3f}",

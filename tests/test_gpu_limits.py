@@ -13,8 +13,7 @@ import torch
 
 import io_aware_softmax_04_amd as iofa
 import oracle
-from helpers import assert_parity, oracle_rows, sample_rows, widen
-from test_gpu_fp8 import _derived_bound
+from helpers import assert_parity, check_backward, fp8_output_bound, oracle_rows, sample_rows, widen
 from workloads import default_scale, make_qkv, make_qkv_fp8
 
 pytestmark = pytest.mark.gpu
@@ -67,7 +66,7 @@ def test_fp8_longest_sequence(dev):
     rows = sample_rows(N_LONG, seed=3, edge=8, middle=16)
     o_ref, lse_ref = oracle.fp8_attention_rows(q8.numpy(), k8.numpy(), v8.numpy(), scale,
                                                sq, sk, sv, rows)
-    bound, eps = _derived_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=rows)
+    bound, eps = fp8_output_bound(q8, k8, v8, scale, sq, sk, sv, o_ref, rows=rows)
     err = np.abs(widen(o[:, :, rows].cpu()) - o_ref)
     print(f"fp8 N=2^20: worst err/bar={np.max(err / bound):.3f}", flush=True)
     assert (err <= bound).all()
@@ -77,8 +76,7 @@ def test_fp8_longest_sequence(dev):
 
 def test_backward_at_the_benchmark_head_shape(dev):
     # two heads of the benchmarked shape (N = 4096, d = 128), full gradients
-    from test_gpu_backward import _run_and_check
-    _run_and_check(1, 2, 4096, 128, "bf16", seed=4096, dev=dev, label="bf16 H2 N4096")
+    check_backward(1, 2, 4096, 128, "bf16", seed=4096, dev=dev, label="bf16 H2 N4096")
 
 
 def test_softmax_longest_rows(dev):
