@@ -378,9 +378,11 @@ def read_traffic(spec):
 
 def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
     """Run ``fn`` warmup times (then keep running it until ``warm_seconds``
-    have passed, so the GPU's clock has settled under load), then steps
-    times; returns (wall ms per step, mean launch ms from HIP events recorded
-    on the launch stream around each call)."""
+    have passed, so the GPU's clock has settled under load), then time
+    ``steps`` back-to-back calls between two synchronisations (wall clock,
+    nothing else queued between the launches), then ``steps`` more calls
+    with HIP events recorded on the launch stream around each one.  Returns
+    (wall ms per step, mean launch ms from the events)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -389,16 +391,19 @@ def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
         for _ in range(8):
             fn()
         torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    t0 = time.perf_counter()
     for a, b in evs:
         a.record(stream)
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     ev = sum(a.elapsed_time(b) for a, b in evs) / steps
     return wall, ev
 
