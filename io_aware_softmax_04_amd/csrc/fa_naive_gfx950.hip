@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kQRows = 128;        // query rows per workgroup (4 waves x 32)
 constexpr int kKeysPerWg = 256;    // keys per workgroup in kernel 1
-constexpr int kMaxChunks = 16;     // 8-element chunks per thread in kernel 2
+constexpr int kMaxChunks = 16;     // 8-element chunks per thread in kernel 2 (N <= 32768)
 
 // ------------------------------------------------ element access (kernel 2)
 
@@ -130,7 +130,10 @@ __global__ __launch_bounds__(256) void naive_scores_16(
 
 // --------------------------------------------------------- kernel 2 (all)
 
-template <class E>
+// MAXC: 8-element chunks per thread the row needs (a power of two, at most
+// kMaxChunks); instances for short rows hold fewer registers, so more rows
+// are in flight per CU.
+template <class E, int MAXC>
 __global__ __launch_bounds__(256) void naive_softmax_16(
     const uint16_t* __restrict__ S, uint16_t* __restrict__ P, float* __restrict__ LSE,
     int N, int ldS) {
@@ -139,10 +142,10 @@ __global__ __launch_bounds__(256) void naive_softmax_16(
   const uint16_t* s = S + row * ldS;
   uint16_t* p = P + row * ldS;
   const int nch = ldS / 8;
-  float v[kMaxChunks][8];
+  float v[MAXC][8];
   float mx = -__builtin_inff();
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nch) {
       load8_16<E>(s + c * 8, v[i]);
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void naive_softmax_16(
   mx = block_reduce(mx, true, red);
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nch) {
 #pragma unroll
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(256) void naive_softmax_16(
   sum = block_reduce(sum, false, red);
   const float inv = 1.0f / sum;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < MAXC; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c < nch) {
       float w[8];
@@ -321,6 +324,24 @@ __global__ __launch_bounds__(256) void naive_pv_f32(
 
 // ---------------------------------------------------------------- launch
 
+template <class E, int MAXC>
+hipError_t launch_naive_softmax16_c(const NaiveArgs& a, int N, int ldS) {
+  hipLaunchKernelGGL((naive_softmax_16<E, MAXC>), dim3(static_cast<unsigned>(a.f.BH * N)),
+                     dim3(256), 0, a.f.stream, static_cast<const uint16_t*>(a.S),
+                     static_cast<uint16_t*>(a.P), a.f.LSE, N, ldS);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_naive_softmax16(const NaiveArgs& a, int N, int ldS) {
+  const int per_thread = (ldS / 8 + 255) / 256;   // chunks per thread the row needs
+  if (per_thread <= 1) return launch_naive_softmax16_c<E, 1>(a, N, ldS);
+  if (per_thread <= 2) return launch_naive_softmax16_c<E, 2>(a, N, ldS);
+  if (per_thread <= 4) return launch_naive_softmax16_c<E, 4>(a, N, ldS);
+  if (per_thread <= 8) return launch_naive_softmax16_c<E, 8>(a, N, ldS);
+  return launch_naive_softmax16_c<E, kMaxChunks>(a, N, ldS);
+}
+
 template <class T, class E, int D>
 hipError_t launch_naive16(const NaiveArgs& a) {
   const FwdArgs& f = a.f;
@@ -333,10 +354,7 @@ hipError_t launch_naive16(const NaiveArgs& a) {
                      static_cast<uint16_t*>(a.S), N, ldS, qtiles, ktiles, wg1, f.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((naive_softmax_16<E>), dim3(static_cast<unsigned>(f.BH * N)), dim3(256), 0,
-                     f.stream, static_cast<const uint16_t*>(a.S), static_cast<uint16_t*>(a.P),
-                     f.LSE, N, ldS);
-  e = hipGetLastError();
+  e = launch_naive_softmax16<E>(a, N, ldS);
   if (e != hipSuccess) return e;
   const int wg3 = static_cast<int>(f.BH * qtiles);
   hipLaunchKernelGGL((naive_pv_16<T, D>), dim3(wg3), dim3(256), 0, f.stream,
