@@ -72,8 +72,9 @@ __global__ __launch_bounds__(256) void naive_scores_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     uint16_t* __restrict__ S, int N, int ldS, int qtiles, int ktiles, int num_wg,
     float scale) {
-  constexpr int BC = 64, KS = D + 8;
+  constexpr int BC = 64, KS = D + 8, SS = BC + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ss[kQRows * SS];   // one S block
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_logical_id(blockIdx.x, num_wg);
@@ -88,8 +89,6 @@ __global__ __launch_bounds__(256) void naive_scores_16(
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = (q < N) ? gmem_vec8<T>(Q + head + static_cast<size_t>(q) * D + 16 * kk + 8 * hi)
                      : __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
-  uint16_t* Srow = S + (static_cast<size_t>(bh) * N + q) * ldS;
-
   for (int sub = 0; sub < kKeysPerWg / BC; ++sub) {
     const int k0 = kt * kKeysPerWg + sub * BC;
     if (k0 >= N) break;
@@ -103,26 +102,29 @@ __global__ __launch_bounds__(256) void naive_scores_16(
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
         s[sb] = T::mfma(lds_vec8<T>(Ks + (32 * sb + l32) * KS + 16 * kk + 8 * hi), qf[kk], s[sb]);
-    if (q < N) {
+    // the block's scores (query rows x 64 keys) go through LDS so that each
+    // row is written as contiguous 16-byte pieces
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int key = k0 + 32 * sb + 8 * g + 4 * hi;
-          uint16_t b[4];
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack2(T::bits(s[sb][4 * g + 0] * scale), T::bits(s[sb][4 * g + 1] * scale));
+        w[1] = pack2(T::bits(s[sb][4 * g + 2] * scale), T::bits(s[sb][4 * g + 3] * scale));
+        *reinterpret_cast<u32x2*>(Ss + (wave * 32 + l32) * SS + 32 * sb + 8 * g + 4 * hi) = w;
+      }
+    __syncthreads();
+    constexpr int CPR = BC / 8;                         // 16-byte pieces per row
 #pragma unroll
-          for (int i = 0; i < 4; ++i) b[i] = T::bits(s[sb][4 * g + i] * scale);
-          if (key + 3 < N) {
-            u32x2 w;
-            w[0] = pack2(b[0], b[1]);
-            w[1] = pack2(b[2], b[3]);
-            *reinterpret_cast<u32x2*>(Srow + key) = w;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (key + i < N) Srow[key + i] = b[i];
-          }
-        }
+    for (int i = 0; i < kQRows * CPR / 256; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / CPR, key = k0 + 8 * (c % CPR);
+      const int qr = qt * kQRows + r;
+      // ldS is a multiple of 8, so a piece that starts before ldS ends there
+      // at the latest; columns in [N, ldS) are never read as scores
+      if (qr < N && key < ldS)
+        *reinterpret_cast<u32x4*>(S + (static_cast<size_t>(bh) * N + qr) * ldS + key) =
+            *reinterpret_cast<const u32x4*>(Ss + r * SS + 8 * (c % CPR));
     }
     __syncthreads();
   }
@@ -256,22 +258,37 @@ __global__ __launch_bounds__(256) void naive_pv_16(
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
 
-  for (int k0 = 0; k0 < N; k0 += BC) {
-    VtTile<D, BC, VS, false> vt;
-    vt.load(V + head + static_cast<size_t>(k0) * D, N - k0, tid);
-    vt.store(Vt, tid);
-    __syncthreads();
+  // P fragments and V rows of the next key tile are loaded while the
+  // current tile is multiplied
+  using vec8 = typename T::vec8;
+  auto load_p = [&](int k0, vec8 (&pf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kidx = k0 + 16 * ks + 8 * hi;
-      const auto pf = (q < N && kidx < ldS)
-                          ? gmem_vec8<T>(Prow + kidx)
-                          : __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-        o[cb] = T::mfma(lds_vec8<T>(Vt + (32 * cb + l32) * VS + 16 * ks + 8 * hi), pf, o[cb]);
+      pf[ks] = (q < N && kidx < ldS) ? gmem_vec8<T>(Prow + kidx)
+                                     : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  VtTile<D, BC, VS, false> vt;
+  vec8 pcur[4], pnext[4];
+  vt.load(V + head, N, tid);
+  load_p(0, pcur);
+  for (int k0 = 0; k0 < N; k0 += BC) {
+    vt.store(Vt, tid);
+    if (k0 + BC < N) {
+      vt.load(V + head + static_cast<size_t>(k0 + BC) * D, N - k0 - BC, tid);
+      load_p(k0 + BC, pnext);
     }
     __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+        o[cb] = T::mfma(lds_vec8<T>(Vt + (32 * cb + l32) * VS + 16 * ks + 8 * hi), pcur[ks], o[cb]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pcur[ks] = pnext[ks];
   }
   if (q < N) {
     uint16_t* Oq = O + head + static_cast<size_t>(q) * D;
