@@ -35,6 +35,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_sched.h"
 
 namespace iofa {
 
@@ -185,6 +186,16 @@ using P0 = std::integral_constant<int, 0>;
 using P1 = std::integral_constant<int, 1>;
 
 // --------------------------------------------------------------- dQ kernel
+//
+// Per wave (32 query rows) and 32-key tile t: S^T_t and dP^T_t (MFMA), then
+// P_t and dS_t (vector unit), then dQ^T += K_t^T dS^T_t (MFMA).  The loop is
+// software-pipelined like the fused forward: iteration j computes P_j, dS_j
+// while the matrix cores run dQ for tile j-1 and S^T, dP^T for tile j+1.  K
+// tile t is read in iterations t-1 (scores) and t+1 (transposed, for dQ) and
+// copied in iteration t-2, so K has four LDS stages; V tile t is read in
+// iteration t-1 only (two stages).  Score and dP registers alternate between
+// two sets by tile parity; the loop is unrolled by four so every stage offset
+// is an immediate.
 
 template <class T, int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   using vec8 = typename T::vec8;
   constexpr int BC = kBwdTile;
   constexpr uint32_t TB = BC * D * 2u;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * BC * D];   // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[6 * BC * D];   // K0..K3 V0 V1
   const uint32_t sm = lds_address(smem);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -213,8 +224,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   LaneOffsets<D> lo;
   lo.init(lane, 0);
   const int NT = (N + BC - 1) / BC;
-  kcp.copy(K + head, 0, N, sm);
-  vcp.copy(V + head, 0, N, sm + 2 * TB);
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  auto copy_tile = [&](int t) {   // K_t -> K stage t % 4, V_t -> V stage t % 2
+    kcp.copy(Kh, t * BC, N, sm + (t & 3) * TB);
+    vcp.copy(Vh, t * BC, N, sm + (4 + (t & 1)) * TB);
+  };
+  copy_tile(0);
+  if (NT > 1) copy_tile(1);
 
   vec8 qf[D / 16], df[D / 16];
   load_row_frags<T, D>(qf, Q + head + static_cast<size_t>(q) * D, qv, hi);
@@ -226,37 +243,105 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb) acc[cb] = f32x16{};
 
-  // tile j in stage j % 2; the copies of tile j+1 are in flight meanwhile
-  auto tile = [&](auto par, int j) {
-    constexpr int P = decltype(par)::value;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 < NT) {
-      kcp.copy(K + head, (j + 1) * BC, N, sm + (1 - P) * TB);
-      vcp.copy(V + head, (j + 1) * BC, N, sm + (3 - P) * TB);
-    }
-    f32x16 s = f32x16{}, dp = f32x16{};
-    rows_times<T, D>(s, sm + P * TB, lo, qf);          // S^T  (keys x queries)
-    rows_times<T, D>(dp, sm + (2 + P) * TB, lo, df);   // dP^T
-    const int kvalid = N - j * BC;
+  // score / dP register sets by tile parity, packed dS by tile parity
+  f32x16 s_[2], dp_[2];
+  vec8 pk_[2][2];
+
+  // S^T_t, dP^T_t into set t % 2 (K stage KS, V stage VS)
+  auto scores = [&](auto set, auto ks, auto vs) {
+    constexpr int SET = decltype(set)::value, KS = decltype(ks)::value, VS = decltype(vs)::value;
+    s_[SET] = f32x16{};
+    dp_[SET] = f32x16{};
+    rows_times<T, D>(s_[SET], sm + KS * TB, lo, qf);          // S^T  (keys x queries)
+    rows_times<T, D>(dp_[SET], sm + (4 + VS) * TB, lo, df);   // dP^T
+  };
+  // P_t, dS_t of set SET, packed; TAIL masks keys at or beyond kvalid
+  auto softmax_ds = [&](auto set, auto tail, int kvalid) {
+    constexpr int SET = decltype(set)::value;
+    constexpr bool TAIL = decltype(tail)::value;
     f32x16 ds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
-      float p = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
-      p = key < kvalid ? p : 0.f;
-      ds[r] = p * (dp[r] - Dq);
+      float p = __builtin_amdgcn_exp2f(fmaf(s_[SET][r], c2, -lse2));
+      if (TAIL) {
+        const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
+        p = key < kvalid ? p : 0.f;
+      }
+      ds[r] = p * (dp_[SET][r] - Dq);
     }
-    vec8 pk[2];
-    pack_b<T>(ds, pk);
-    cols_times<T, D>(acc, sm + P * TB, lo, pk);        // dQ^T += K^T dS^T
+    pack_b<T>(ds, pk_[SET]);
   };
-  int j = 0;
-  for (; j + 1 < NT; j += 2) {
-    tile(P0{}, j);
-    tile(P1{}, j + 1);
+  // dQ^T += K_t^T dS^T_t, K_t in stage KS, dS_t in set SET
+  auto dq_update = [&](auto set, auto ks) {
+    constexpr int SET = decltype(set)::value, KS = decltype(ks)::value;
+    cols_times<T, D>(acc, sm + KS * TB, lo, pk_[SET]);
+  };
+  auto bottom = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using NoTail = std::integral_constant<bool, false>;
+  using Tail = std::integral_constant<bool, true>;
+  constexpr int NM = 3 * (D / 16);                 // products per middle iteration
+  constexpr int NRD = 2 * (D / 16) + 2 * (D / 16); // 2 b128 per score step, 2 transposed per dQ step
+
+  // middle iteration j (0 < j < NT-1), J = j % 4
+  auto middle = [&](auto jm, int j) {
+    constexpr int J = decltype(jm)::value;
+    using Cur = std::integral_constant<int, J % 2>;
+    using Nxt = std::integral_constant<int, (J + 1) % 2>;
+    if (j + 2 < NT) copy_tile(j + 2);
+    softmax_ds(Cur{}, NoTail{}, BC);
+    dq_update(Nxt{}, std::integral_constant<int, (J + 3) % 4>{});    // tile j-1
+    scores(Nxt{}, std::integral_constant<int, (J + 1) % 4>{},
+           std::integral_constant<int, (J + 1) % 2>{});             // tile j+1
+    interleave_mfma_valu<NM, NRD, 4, 3>();
+    bottom();
+  };
+  // last iteration j = NT-1 (> 0), J = j % 4: no copies, no scores
+  auto last = [&](auto jm, int j) {
+    constexpr int J = decltype(jm)::value;
+    using Cur = std::integral_constant<int, J % 2>;
+    using Prv = std::integral_constant<int, (J + 1) % 2>;
+    softmax_ds(Cur{}, Tail{}, N - j * BC);
+    dq_update(Prv{}, std::integral_constant<int, (J + 3) % 4>{});    // tile j-1
+    dq_update(Cur{}, std::integral_constant<int, J>{});              // tile j
+  };
+
+  bottom();                                        // tiles 0 and 1 are in LDS
+  scores(I0{}, I0{}, I0{});                        // tile 0
+  if (NT == 1) {
+    softmax_ds(I0{}, Tail{}, N);
+    dq_update(I0{}, I0{});
+  } else {
+    // iteration 0: P_0, dS_0 with the scores of tile 1
+    if (NT > 2) copy_tile(2);
+    softmax_ds(I0{}, NoTail{}, BC);
+    scores(I1{}, I1{}, I1{});
+    interleave_mfma_valu<2 * (D / 16), 2 * (D / 16), 4, 3>();
+    bottom();
+    int j = 1;
+    for (; j + 4 <= NT - 1; j += 4) {
+      middle(I1{}, j);
+      middle(I2{}, j + 1);
+      middle(I3{}, j + 2);
+      middle(I0{}, j + 3);
+    }
+    // j % 4 == 1 here; at most three middle iterations remain
+    if (j < NT - 1) { middle(I1{}, j); ++j; }
+    if (j < NT - 1) { middle(I2{}, j); ++j; }
+    if (j < NT - 1) { middle(I3{}, j); ++j; }
+    switch (j & 3) {
+      case 0: last(I0{}, j); break;
+      case 1: last(I1{}, j); break;
+      case 2: last(I2{}, j); break;
+      default: last(I3{}, j); break;
+    }
   }
-  if (j < NT) tile(P0{}, j);
   if (qv) store_rowmajor<T, D>(dQ + head + static_cast<size_t>(q) * D, acc, hi, scale);
   __builtin_amdgcn_s_waitcnt(0);
 }
