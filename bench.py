@@ -724,6 +724,16 @@ def main():
             if rnd:
                 line["mfma_ceiling"]["fused_frac_of_bf16_random_ceiling"] = round(
                     achieved / rnd[0]["tflops"], 4)
+            ex = [c for c in cases if c["case"].startswith("v_exp_f32")]
+            if ex:
+                # one exponential per score: B*H*N^2 of them at the chip's
+                # measured v_exp_f32 rate is a floor under the fused kernel
+                n_exp = float(B * H * N * N)
+                floor_ms = n_exp / ex[0]["lane_ops_per_s"] * 1e3
+                line["exp_floor"] = {"exponentials": n_exp,
+                                     "rate_per_s": ex[0]["lane_ops_per_s"],
+                                     "ms": round(floor_ms, 4),
+                                     "frac_of_fused_launch": round(floor_ms / ev_ms, 4)}
             print(f"[bench] MFMA ceiling: {line['mfma_ceiling']}", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:

@@ -7,7 +7,10 @@
 // operands are either one constant pair per lane or eight pairs of random
 // values (random signs and mantissas, as attention inputs have) used in
 // rotation.  Prints one JSON line per case: TFLOP/s from HIP events and the
-// shader clock from the cycle and real-time counters of one wave.
+// shader clock from the cycle and real-time counters of one wave.  Two more
+// cases give the vector unit's rates at the same occupancy, in lane
+// operations per second: v_exp_f32 (the exponential every attention score
+// needs) and v_fma_f32, each on eight independent dependency chains.
 //
 // Standalone measurement program (not part of libiofa.so).  Every lane
 // writes only out[blockIdx.x * blockDim.x + threadIdx.x]; lane 0 of block 0
@@ -128,6 +131,33 @@ __global__ __launch_bounds__(256, 2) void fp8_kernel(float* out, int iters,
   }
 }
 
+// NCH independent chains of v_exp_f32 (x <- -exp2(x) stays in [-1, -0.5])
+// or v_fma_f32 (x <- 0.999 x + 0.001 stays near 1).
+template <bool EXP>
+__global__ __launch_bounds__(256, 2) void valu_kernel(float* out, int iters,
+                                                      unsigned long long* clk) {
+  constexpr int NCH = 8;
+  const unsigned id = blockIdx.x * blockDim.x + threadIdx.x;
+  float x[NCH];
+  for (int j = 0; j < NCH; ++j) x[j] = -0.6f - 0.01f * j - 1e-7f * (id & 1023);
+  const unsigned long long c0 = __builtin_readcyclecounter();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+      x[j] = EXP ? -__builtin_amdgcn_exp2f(x[j]) : __builtin_fmaf(x[j], 0.999f, 0.001f);
+  }
+  const unsigned long long c1 = __builtin_readcyclecounter();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+  for (int j = 0; j < NCH; ++j) s += x[j];
+  out[id] = s;
+  if (id == 0) {
+    clk[0] = c1 - c0;
+    clk[1] = r1 - r0;
+  }
+}
+
 typedef void (*KernelFn)(float*, int, unsigned long long*);
 
 void run(const char* name, KernelFn fn, double flops_per_mfma, int mfma_per_iter,
@@ -157,6 +187,32 @@ void run(const char* name, KernelFn fn, double flops_per_mfma, int mfma_per_iter
   CHECK(hipEventDestroy(e1));
 }
 
+void run_valu(const char* name, KernelFn fn, float* out, unsigned long long* clk, int blocks,
+              int iters) {
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, 0, out, 2, clk);   // warm-up
+  CHECK(hipDeviceSynchronize());
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  CHECK(hipEventRecord(e0));
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, 0, out, iters, clk);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  CHECK(hipGetLastError());
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  unsigned long long h[2];
+  CHECK(hipMemcpy(h, clk, sizeof(h), hipMemcpyDeviceToHost));
+  const double lane_ops = 8.0 * iters * 256.0 * blocks;
+  const double mhz = h[1] ? 100.0 * static_cast<double>(h[0]) / static_cast<double>(h[1]) : 0.0;
+  std::printf("{\"case\": \"%s\", \"ms\": %.3f, \"lane_ops_per_s\": %.4e, "
+              "\"lanes_per_clock_per_simd\": %.2f, \"shader_clock_mhz\": %.0f}\n",
+              name, ms, lane_ops / (ms * 1e-3),
+              mhz > 0 ? lane_ops / (ms * 1e-3) / (1024.0 * mhz * 1e6) : 0.0, mhz);
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+}
+
 }  // namespace
 
 int main() {
@@ -172,6 +228,8 @@ int main() {
       clk, blocks, 2500);
   run("fp8 e4m3 32x32x64, 8 random operand pairs", fp8_kernel<8>, fp8_mfma, 8 * kAcc, 5033.2, out,
       clk, blocks, 1250);
+  run_valu("v_exp_f32, 8 chains per lane", valu_kernel<true>, out, clk, blocks, 20000);
+  run_valu("v_fma_f32, 8 chains per lane", valu_kernel<false>, out, clk, blocks, 40000);
   CHECK(hipFree(out));
   CHECK(hipFree(clk));
   return 0;
