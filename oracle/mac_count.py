@@ -1,15 +1,15 @@
 """Element-access count of standard three-step attention -- TEST INFRASTRUCTURE.
 
-A CPU mirror of the three lines [ctyun] "MAC分析 / 标准Transformer MAC分析"
-analyses, run against a counting stand-in for HBM.  Each line loads its input
-matrices from the stand-in once and stores its output once, exactly as that
-section assumes ("per float" accessed):
+A CPU mirror of the three steps of standard attention that [ctyun]
+"MAC分析 / 标准Transformer MAC分析" analyses, run against a counting stand-in
+for HBM.  Each step loads its input matrices from the stand-in once and stores
+its output once, exactly as that section assumes ("per float" accessed):
 
-  line 1: read Q, K; S = scale * Q K^T; write S
-  line 2: read S; P = softmax(S) (row-wise, safe form); write P
-  line 3: read P, V; O = P V; write O
+  first step:  read Q, K; S = scale * Q K^T; write S
+  second step: read S; P = softmax(S) (row-wise, safe form); write P
+  third step:  read P, V; O = P V; write O
 
-The page's per-line totals (2Nd + N^2, 2N^2, N^2 + 2Nd; sum 4Nd + 4N^2) are
+The page's per-step totals (2Nd + N^2, 2N^2, N^2 + 2Nd; sum 4Nd + 4N^2) are
 pinned by a test against these counts; the arithmetic is the same definition
 as ``standard_attention`` and is checked against it.  The initial placement
 of Q, K, V in the stand-in is not counted (the inputs are already resident).
@@ -42,28 +42,28 @@ class CountingHBM:
 
 
 def standard_attention_mac(q, k, v, scale):
-    """One head: q, k (N, d), v (N, dv).  Returns (O, per_line) where
-    per_line is a list of three (reads, writes) element counts."""
+    """One head: q, k (N, d), v (N, dv).  Returns (O, per_step) where
+    per_step is a list of three (reads, writes) element counts."""
     hbm = CountingHBM()
     hbm.place("Q", q)
     hbm.place("K", k)
     hbm.place("V", v)
-    per_line = []
+    per_step = []
 
     r0, w0 = hbm.reads, hbm.writes
     qm, km = hbm.read("Q"), hbm.read("K")
     hbm.write("S", scale * (qm @ km.T))
-    per_line.append((hbm.reads - r0, hbm.writes - w0))
+    per_step.append((hbm.reads - r0, hbm.writes - w0))
 
     r0, w0 = hbm.reads, hbm.writes
     s = hbm.read("S")
     f = np.exp(s - s.max(axis=1, keepdims=True))
     hbm.write("P", f / f.sum(axis=1, keepdims=True))
-    per_line.append((hbm.reads - r0, hbm.writes - w0))
+    per_step.append((hbm.reads - r0, hbm.writes - w0))
 
     r0, w0 = hbm.reads, hbm.writes
     p, vm = hbm.read("P"), hbm.read("V")
     hbm.write("O", p @ vm)
-    per_line.append((hbm.reads - r0, hbm.writes - w0))
+    per_step.append((hbm.reads - r0, hbm.writes - w0))
 
-    return hbm.read("O"), per_line
+    return hbm.read("O"), per_step

@@ -361,13 +361,13 @@ def test_mac_count_matches_printed_formulas(N, d):
         g = json.load(fh)
     rng = np.random.default_rng(N * 100 + d)
     q, k, v = (rng.normal(size=(N, d)) for _ in range(3))
-    o, per_line = oracle.standard_attention_mac(q, k, v, 0.5)
-    for (reads, writes), spec in zip(per_line, g["per_line"]):
+    o, per_step = oracle.standard_attention_mac(q, k, v, 0.5)
+    for (reads, writes), spec in zip(per_step, g["per_step"]):
         assert reads == sum(_eval(e, N, d) for e in spec["reads"].values())
         assert writes == sum(_eval(e, N, d) for e in spec["writes"].values())
         assert reads + writes == _eval(spec["printed_total"], N, d)
-    assert sum(r + w for r, w in per_line) == _eval(g["printed_sum"], N, d)
-    transfers = sum(len(s["reads"]) + len(s["writes"]) for s in g["per_line"])
+    assert sum(r + w for r, w in per_step) == _eval(g["printed_sum"], N, d)
+    transfers = sum(len(s["reads"]) + len(s["writes"]) for s in g["per_step"])
     assert transfers == g["matrix_transfers"]
     o_ref, _ = _oracle_one_head(q, k, v, 0.5)
     np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
