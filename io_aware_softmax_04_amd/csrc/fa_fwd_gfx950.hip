@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv<1 - P>(p_prev);
     ws.template scores<1 - P>(s_nxt);
-    interleave_mfma_valu<NM, NRD, 4, 4>();
+    interleave_mfma_valu<NM, NRD, 6, 4>();
     bottom(ws.commit_lazy(rs, s_cur, p_cur, c2));
   };
   // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
