@@ -354,6 +354,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(
   constexpr int NM = C::CB + 2 * C::KB;         // products per iteration
   constexpr int NRD = 4 * C::KB + 4 * C::CB;    // LDS reads per iteration
   constexpr int VPM = D == 128 ? 14 : 28;       // vector instructions per product
+  // LDS reads issued ahead of the interleaved products (more is faster until
+  // the registers they need run out)
+  constexpr int LEAD = NRD < 16 ? NRD : 16;
   auto bottom = [&](float alpha) {
     ws.rescale(alpha);
     __builtin_amdgcn_s_waitcnt(0);
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv<1 - P>(p_prev);
     ws.template scores<1 - P>(s_nxt);
-    interleave_mfma_valu<NM, NRD, 4, VPM>();
+    interleave_mfma_valu<NM, NRD, LEAD, VPM>();
     bottom(ws.commit_lazy(rs, s_cur, p_cur, c2));
   };
   auto last = [&](auto par, int j, f32x16 (&s_cur)[2], i32x8& p_prev, i32x8& p_cur) {
