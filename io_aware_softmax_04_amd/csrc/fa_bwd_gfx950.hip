@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     dq_update(Nxt{}, std::integral_constant<int, (J + 3) % 4>{});    // tile j-1
     scores(Nxt{}, std::integral_constant<int, (J + 1) % 4>{},
            std::integral_constant<int, (J + 1) % 2>{});             // tile j+1
-    interleave_mfma_valu<NM, NRD, 4, 3>();
+    interleave_mfma_valu<NM, NRD, 8, 3>();
     bottom();
   };
   // last iteration j = NT-1 (> 0), J = j % 4: no copies, no scores
