@@ -16,7 +16,8 @@
 //                the lane owning a query column), P^T and dS^T in-lane,
 //                dQ^T += K^T dS^T with dS^T straight from registers and K^T
 //                read through ds_read_b64_tr_b16 -- the shape of the fused
-//                forward's P V;
+//                forward's P V; software-pipelined across tiles like the
+//                forward (see the kernel);
 //   bwd_dkdv     one workgroup per 128 keys (4 waves x 32), Q and dO tiles
 //                of 32 queries (with their (L log2 e, D) pairs) streamed;
 //                per tile S = Q K^T and dP = dO V^T with the lane owning a
@@ -28,9 +29,10 @@
 // against the 5 a single pass with atomic dQ updates would need) so that no
 // output is shared between workgroups and the result is deterministic.
 // Tiles that are read both as row fragments and transposed use the kv_swz
-// swizzle; copies are buffer_load ... lds into two stages, the next tile's
-// copies in flight while the current one is computed; the tile loop is
-// unrolled by two so stage offsets are immediates.
+// swizzle; copies are buffer_load ... lds into LDS stages with later tiles'
+// copies in flight while the current one is computed; the tile loops are
+// unrolled (by four in bwd_dq, by two in bwd_dkdv) so stage offsets are
+// immediates.
 #include <type_traits>
 
 #include "fa_device.h"
