@@ -542,6 +542,15 @@ def fp8_measure(spec, args, torch, iofa, dev):
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)}}
 
 
+def device_info(torch, dev):
+    """What the runtime reports for the device the run used."""
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1),
+            "hip_runtime": getattr(torch.version, "hip", None)}
+
+
 def mfma_ceiling():
     """Run the standalone MFMA-ceiling program (a child process) and return
     its cases: the sustained bf16 and fp8 MFMA rates of the whole chip at the
@@ -664,6 +673,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
         "fused_launch_ms": round(ev_ms, 5),
+        "device": device_info(torch, dev),
         "bytes_models": models,
     }
 
