@@ -44,8 +44,10 @@ def test_backward_larger_and_multi_head(dev):
     check_backward(2, 3, 1000, 128, "bf16", seed=1, dev=dev, label="bf16 B2 H3 N1000")
 
 
-def test_backward_stress_distribution(dev):
-    check_backward(1, 2, 500, 128, "fp16", seed=2, dev=dev, dist="stress", label="stress fp16")
+@pytest.mark.parametrize("dtype,d", [("fp16", 128), ("bf16", 128), ("bf16", 64)])
+def test_backward_stress_distribution(dtype, d, dev):
+    check_backward(1, 2, 500, d, dtype, seed=2 + d, dev=dev, dist="stress",
+                   label=f"stress {dtype} d={d}")
 
 
 def test_backward_is_deterministic(dev):
