@@ -97,15 +97,6 @@ __device__ inline int xcd_logical_id(int w, int G) {
   return x * q + (x < rem ? x : rem) + s;
 }
 
-// Position of key j (0..63 inside a 64-key tile) in a transposed V row, such
-// that the 8 keys a lane multiplies in one 32x32x16 product of P V sit in 16
-// consecutive bytes.  The score accumulator gives lane-half h, register r of
-// a 32-key block the key 8*(r/4) + 4*h + r%4; taking registers 8*t .. 8*t+7
-// as the k-slots of key step t swaps bits 2 and 3 of the key index.
-__device__ inline int vt_pos(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
 // ------------------------------------------------------------ tile loads
 
 // K (or Q) tile of BC rows x D 16-bit elements into LDS rows of stride KS
@@ -144,11 +135,9 @@ struct RowTile {
 // V tile of BC keys x D 16-bit elements, stored transposed in LDS as D rows
 // of stride VS elements (one row per output column c, keys along the row).
 // Each thread loads KPB consecutive keys of one 16-byte column chunk and
-// writes, for each of its 8 columns, KPB keys as one KPB*2-byte store.
-// With PERM the keys are placed at vt_pos(j) (fused path, P from registers);
-// otherwise in natural order (naive path, P from memory).  Keys at or beyond
-// `rows_valid` are zeros.
-template <int D, int BC, int VS, bool PERM>
+// writes, for each of its 8 columns, KPB keys (in natural order) as one
+// KPB*2-byte store.  Keys at or beyond `rows_valid` are zeros.
+template <int D, int BC, int VS>
 struct VtTile {
   static constexpr int CH = D / 8;
   static constexpr int KPB = BC * CH / 256;
@@ -170,8 +159,7 @@ struct VtTile {
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
     const int kg = tid % NKG, cc = tid / NKG;
-    const int j0 = kg * KPB;
-    const int pos = PERM ? vt_pos(j0) : j0;
+    const int pos = kg * KPB;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint16_t* dst = lds + (cc * 8 + e) * VS + pos;
@@ -267,16 +255,6 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t byt
 
 __device__ inline uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(IOFA_LDS(const void, p)));
-}
-
-// s_waitcnt with only the vector-memory counter constrained: wait until at
-// most n vector memory operations of this wave are outstanding.
-template <int n>
-__device__ inline void wait_vmem() {
-  static_assert(n >= 0 && n < 64, "vmcnt out of range");
-  // gfx9 encoding: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8]
-  // (15 = no wait), vmcnt[5:4] in bits 15:14
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
 // Per-lane part of the direct copies of one K or V tile (BC rows x D 16-bit

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void naive_pv_16(
                                      : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
     }
   };
-  VtTile<D, BC, VS, false> vt;
+  VtTile<D, BC, VS> vt;
   vec8 pcur[4], pnext[4];
   vt.load(V + head, N, tid);
   load_p(0, pcur);
