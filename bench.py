@@ -382,7 +382,8 @@ def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
     ``steps`` back-to-back calls between two synchronisations (wall clock,
     nothing else queued between the launches), then ``steps`` more calls
     with HIP events recorded on the launch stream around each one.  Returns
-    (wall ms per step, mean launch ms from the events)."""
+    (wall ms per step, mean launch ms from the events, the events' median
+    and minimum in ms)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -404,8 +405,9 @@ def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    ev = sum(a.elapsed_time(b) for a, b in evs) / steps
-    return wall, ev
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    ev = sum(times) / steps
+    return wall, ev, times[steps // 2], times[0]
 
 
 def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
@@ -472,9 +474,9 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
                      dtype=torch.uint8, device=dev)
     flops = 4.0 * B * H * N * N * d
     steps = max(5, min(args.steps, 30))
-    _, f_ms = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch,
+    _, f_ms, *_ = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch,
                             warm_seconds=0.3)
-    _, s_ms = time_launches(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g),
+    _, s_ms, *_ = time_launches(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g),
                             steps, 3, torch, warm_seconds=0.3)
     rows = B * H * N
     flat = ws.view(torch.float32)
@@ -482,7 +484,7 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     lse_part = flat[g * rows * d:g * rows * (d + 1)].view(g, rows)
     o2 = torch.empty((rows, d), dtype=q.dtype, device=dev)
     l2 = torch.empty((rows,), dtype=torch.float32, device=dev)
-    _, m_ms = time_launches(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2),
+    _, m_ms, *_ = time_launches(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2),
                             steps, 3, torch, warm_seconds=0.3)
     merge_bytes = g * rows * (d + 1) * 4 + rows * (d * q.element_size() + 4)
     return {
@@ -512,7 +514,7 @@ def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws = torch.empty(iofa.fa_bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
     steps = max(5, min(args.steps, 30))
-    _, ms = time_launches(lambda: iofa.fa_bwd(qd, kd, vd, o, do, lse, dq, dk, dv, ws, scale),
+    _, ms, *_ = time_launches(lambda: iofa.fa_bwd(qd, kd, vd, o, do, lse, dq, dk, dv, ws, scale),
                           steps, 3, torch, warm_seconds=0.3)
     alg = 10.0 * B * H * N * N * d
     return {"workload": spec["name"], "ms": round(ms, 4),
@@ -533,7 +535,7 @@ def fp8_measure(spec, args, torch, iofa, dev):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     scale = default_scale(d)
     steps = max(5, min(args.steps, 50))
-    _, ms = time_launches(lambda: iofa.fa_fwd_fp8(q8, k8, v8, o, lse, scale, sq, sk, sv),
+    _, ms, *_ = time_launches(lambda: iofa.fa_fwd_fp8(q8, k8, v8, o, lse, scale, sq, sk, sv),
                           steps, min(args.warmup, 5), torch, warm_seconds=0.3)
     tf = 4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12
     return {"workload": f"fp8 (E4M3, per-tensor scales) B{B} H{H} N{N} d{d}, bf16 output",
@@ -566,6 +568,14 @@ def mfma_ceiling():
     return [json.loads(ln) for ln in proc.stdout.splitlines() if ln.startswith("{")]
 
 
+def ceiling_cases(lines):
+    """Split the ceiling program's lines into its measured cases and the
+    device properties it reports first."""
+    cases = [c for c in lines if "case" in c]
+    props = next((c for c in lines if "device" in c), None)
+    return cases, props
+
+
 def softmax_measure(args, torch, iofa, dev):
     """The standalone row softmax on bf16 rows that fit one workgroup (x read
     once, y written once) and on long rows (x read twice).  Roofline: HBM;
@@ -580,7 +590,7 @@ def softmax_measure(args, torch, iofa, dev):
         nb = iofa.fa_softmax_workspace_bytes(rows, n, x.dtype)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         steps = max(5, min(args.steps, 30))
-        _, ms = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
+        _, ms, *_ = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
                               steps, 3, torch, warm_seconds=0.3)
         alg = rows * n * 2 * 2 + rows * 4
         reads = 1 if nb == 0 else 2
@@ -645,9 +655,9 @@ def main():
         iofa.fa_fwd(qd, kd, vd, o, lse, scale)
 
     print(f"[bench] workload {args.workload}: {spec['name']}", file=sys.stderr, flush=True)
-    wall_ms, ev_ms = time_launches(fused, args.steps, args.warmup, torch)
-    print(f"[bench] fused: {wall_ms:.4f} ms/step wall, {ev_ms:.4f} ms/launch (events)",
-          file=sys.stderr, flush=True)
+    wall_ms, ev_ms, ev_med, ev_min = time_launches(fused, args.steps, args.warmup, torch)
+    print(f"[bench] fused: {wall_ms:.4f} ms/step wall, {ev_ms:.4f} ms/launch (events; "
+          f"median {ev_med:.4f}, min {ev_min:.4f})", file=sys.stderr, flush=True)
     achieved = flops / (ev_ms * 1e-3) / 1e12
     value = flops / (wall_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if spec["dtype"] in ("bf16", "fp16") else 157.3
@@ -673,6 +683,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
         "fused_launch_ms": round(ev_ms, 5),
+        "fused_launch_ms_median": round(ev_med, 5),
+        "fused_launch_ms_min": round(ev_min, 5),
+        "fused_tflops_at_median": round(flops / (ev_med * 1e-3) / 1e12, 2),
         "device": device_info(torch, dev),
         "bytes_models": models,
     }
@@ -698,7 +711,7 @@ def main():
                 iofa.fa_naive_fwd(qd, kd, vd, o2, lse2, s_ws, p_ws, scale)
 
             nsteps = max(3, min(args.steps, 20))
-            n_wall, n_ev = time_launches(naive, nsteps, min(args.warmup, 3), torch,
+            n_wall, n_ev, *_ = time_launches(naive, nsteps, min(args.warmup, 3), torch,
                                          warm_seconds=0.3)
             line["naive_contrast"] = {
                 "ms_per_call": round(n_ev, 4),
@@ -727,7 +740,9 @@ def main():
         print(f"[bench] row softmax: {line['softmax_rows']}", file=sys.stderr, flush=True)
 
     if not args.no_ceiling:
-        cases = mfma_ceiling()
+        cases, props = ceiling_cases(mfma_ceiling() or [])
+        if props:
+            line["device"]["hip_properties"] = props
         if cases:
             rnd = [c for c in cases if c["case"].startswith("bf16") and "random" in c["case"]]
             line["mfma_ceiling"] = {"cases": cases}

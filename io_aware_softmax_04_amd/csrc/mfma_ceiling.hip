@@ -217,6 +217,16 @@ void run_valu(const char* name, KernelFn fn, float* out, unsigned long long* clk
 
 int main() {
   const int blocks = 512;   // two workgroups per CU on 256 CUs
+  {
+    // what the runtime reports for device 0: its name and its peak clocks
+    hipDeviceProp_t prop;
+    CHECK(hipGetDeviceProperties(&prop, 0));
+    printf("{\"device\": \"%s\", \"arch\": \"%s\", \"compute_units\": %d, "
+           "\"max_shader_clock_mhz\": %d, \"memory_clock_mhz\": %d, \"memory_bus_bits\": %d}\n",
+           prop.name, prop.gcnArchName, prop.multiProcessorCount, prop.clockRate / 1000,
+           prop.memoryClockRate / 1000, prop.memoryBusWidth);
+    fflush(stdout);
+  }
   float* out = nullptr;
   unsigned long long* clk = nullptr;
   CHECK(hipMalloc(&out, blocks * 256 * sizeof(float)));

@@ -1,0 +1,70 @@
+"""Host-side logic of bench.py that needs no GPU: the algorithmic byte
+models, the launch grid that tells the fused kernel's dispatches apart in a
+trace, the split of the ceiling program's output, and the one-GPU guard."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import WORKLOADS  # noqa: E402
+
+
+# Per workload: compulsory bytes e*4Nd + 4N per head (Q, K, V read once, O and
+# the fp32 LSE written once), the tiled-IO model e*(2Nd + 2Nd*ceil(N/128)) + 4N
+# per head (K and V streamed once per 128-row query tile) and the naive model
+# e*(4Nd + 4N^2) per head (the element count of the three-step standard
+# attention, S and P stored in the input type).  Worked out by hand from those
+# definitions for each workload's shape.
+EXPECTED = {
+    1: (263_168, 394_240, 1_310_720),
+    2: (33_816_576, 151_257_088, 570_425_344),
+    3: (134_742_016, 2_215_116_800, 4_429_185_024),
+    4: (538_968_064, 34_630_270_976, 69_256_347_648),
+    5: (134_725_568, 4_362_067_904, 8_722_038_912),
+}
+
+
+@pytest.mark.parametrize("idx", sorted(EXPECTED))
+def test_byte_models(idx):
+    m = bench.bytes_models(WORKLOADS[idx])
+    assert (m["compulsory"], m["tiled_io_model"], m["naive_model"]) == EXPECTED[idx]
+
+
+def test_byte_models_order():
+    # the tiled model never undercuts the compulsory bytes, and the naive
+    # model exceeds the tiled one whenever N is above the query tile
+    for spec in WORKLOADS.values():
+        m = bench.bytes_models(spec)
+        assert m["compulsory"] <= m["tiled_io_model"] <= m["naive_model"]
+
+
+def test_fused_grid_of_the_benchmark_workload():
+    # B*H*ceil(N/128) workgroups of 256 work-items: 1024 workgroups at
+    # B2 H16 N4096, the grid the kernel trace lists for the fused forward
+    assert bench.fused_grid_items(WORKLOADS[3]) == 1024 * 256
+    assert bench.fused_grid_items(WORKLOADS[5]) == 2 * 8 * 64 * 256
+
+
+def test_ceiling_output_split():
+    lines = [{"device": "X", "max_shader_clock_mhz": 2400},
+             {"case": "bf16 32x32x16, constant operands", "tflops": 1.0},
+             {"case": "v_exp_f32, 8 chains per lane", "lane_ops_per_s": 2.0}]
+    cases, props = bench.ceiling_cases(lines)
+    assert [c["case"] for c in cases] == [lines[1]["case"], lines[2]["case"]]
+    assert props == lines[0]
+    assert bench.ceiling_cases([]) == ([], None)
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                          timeout=120, cwd=ROOT)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+    assert proc.stdout == ""
