@@ -160,11 +160,9 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
         "",
         "```",
         f"rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- "
-        f"python bench.py --workload {index} --steps 3 --warmup 1 "
-        f"--no-cpu-baseline --calibrate-copy-mib {copy_mib}",
+        f"python bench.py --workload {index} {TRAFFIC_BENCH_ARGS} --calibrate-copy-mib {copy_mib}",
         f"rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv -- "
-        f"python bench.py --workload {index} --steps 3 --warmup 1 "
-        f"--no-cpu-baseline --calibrate-copy-mib {copy_mib}",
+        f"python bench.py --workload {index} {TRAFFIC_BENCH_ARGS} --calibrate-copy-mib {copy_mib}",
         f"python bench.py --workload {index} --traffic-from "
         f"{fetch_dir} {write_dir} --copy-mib {copy_mib}",
         "```",
@@ -278,6 +276,9 @@ def summarise_trace(trace_dir, index, spec, bench_args):
     print(path)
 
 
+# the traffic passes run the fused and the naive paths only, a few launches each
+TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-softmax --no-backward --no-fp8 "
+                      "--no-ceiling --no-cpu-baseline")
 SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES"]
 SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
@@ -410,6 +411,37 @@ def time_launches(fn, steps, warmup, torch, warm_seconds=0.0):
     return wall, ev, times[steps // 2], times[0]
 
 
+def time_graph(fn, torch, reps=20, replays=10, warm_seconds=0.3):
+    """Mean duration of one call of ``fn`` when ``reps`` calls are captured
+    in one graph and the graph is replayed ``replays`` times between two
+    events: the calls then run back to back on the GPU, whatever the host
+    side of each call costs, which is what short launches need (from an
+    eager loop the host's per-call cost can exceed the kernel's time)."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        graph.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(replays):
+        graph.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * replays)
+
+
 def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
     """Time the fp64 oracle on a bounded sample (all heads, a prefix of query
     rows sized for about ``target_s`` seconds) and check the GPU output on
@@ -473,23 +505,20 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     ws = torch.empty(max(16, iofa.fa_splitkv_workspace_bytes(B, H, N, d, q.dtype, g)),
                      dtype=torch.uint8, device=dev)
     flops = 4.0 * B * H * N * N * d
-    steps = max(5, min(args.steps, 30))
-    _, f_ms, *_ = time_launches(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), steps, 3, torch,
-                            warm_seconds=0.3)
-    _, s_ms, *_ = time_launches(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g),
-                            steps, 3, torch, warm_seconds=0.3)
+    f_ms = time_graph(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), torch)
+    s_ms = time_graph(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g), torch)
     rows = B * H * N
     flat = ws.view(torch.float32)
     o_part = flat[:g * rows * d].view(g, rows, d)
     lse_part = flat[g * rows * d:g * rows * (d + 1)].view(g, rows)
     o2 = torch.empty((rows, d), dtype=q.dtype, device=dev)
     l2 = torch.empty((rows,), dtype=torch.float32, device=dev)
-    _, m_ms, *_ = time_launches(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2),
-                            steps, 3, torch, warm_seconds=0.3)
+    m_ms = time_graph(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2), torch)
     merge_bytes = g * rows * (d + 1) * 4 + rows * (d * q.element_size() + 4)
     return {
         "workload": f"{spec['dtype']} B{B} H{H} N{N} d{d} (one GPU's share of an 8-way head split)",
         "num_splits": g,
+        "timing": "20 calls captured in a graph, replayed 10 times between two events",
         "fused_ms": round(f_ms, 4), "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1),
         "splitkv_ms": round(s_ms, 4), "splitkv_tflops": round(flops / (s_ms * 1e-3) / 1e12, 1),
         "speedup_splitkv_over_fused": round(f_ms / s_ms, 3),
