@@ -39,9 +39,13 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 int64_t round_up8(int64_t n) { return (n + 7) / 8 * 8; }
 
 // Split-KV policy: at most this many key ranges, and enough of them that the
-// partial pass has about this many workgroups (two per CU on 256 CUs).
+// partial pass has about this many workgroups (two per CU on 256 CUs), but,
+// when G is chosen automatically, no fewer than kMinTilesPerSplit key tiles
+// per range (shorter ranges spend more on the pipeline's fill and drain and on
+// the merge than the extra workgroups win back).
 constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kMinTilesPerSplit = 16;
 constexpr int kMaxMergeParts = 4096;
 
 struct Region {
@@ -157,6 +161,8 @@ int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
     // enough workgroups for one full round at two per CU on 256 CUs
     const int64_t per_split = iofa::fused_workgroups(dtype, B * H, N, 1);
     g = (kTargetWorkgroups + per_split - 1) / per_split;
+    const int64_t longest = tiles / kMinTilesPerSplit;
+    if (g > longest) g = longest;
   }
   if (g > cap) g = cap;
   if (g < 1) g = 1;

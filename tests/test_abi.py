@@ -160,6 +160,12 @@ def test_split_count_policy(lib):
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 128, 2, 99) == 4      # 4 key tiles of 32
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 2, 99) == 2       # 2 key tiles of 64
     assert iofa.fa_splitkv_num_splits(1, 1, 1 << 20, 128, 2, 1000) == 64
+    # automatic G keeps at least 16 key tiles per range: 32 tiles of 32 keys
+    # at N = 1024, d = 128 allow 2 ranges although 64 workgroups ask for 8
+    assert iofa.fa_splitkv_num_splits(4, 2, 1024, 128, 2, 0) == 2
+    assert iofa.fa_splitkv_num_splits(4, 2, 1024, 128, 2, 8) == 8      # an explicit G stays
+    assert iofa.fa_splitkv_num_splits(1, 1, 300, 128, 2, 0) == 1       # 10 tiles: no split
+    assert iofa.fa_splitkv_num_splits(1, 1, 16384, 128, 2, 0) == 4
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 96, 2, 0) == 0        # invalid d
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 5, 0) == 0        # invalid dtype
 
