@@ -108,3 +108,31 @@ def test_naive_forward_in_a_graph(dev):
     p_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     _replays_match(lambda: iofa.fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, default_scale(64)),
                    [o, lse], dev)
+
+
+def test_graph_replay_reads_the_current_inputs(dev):
+    # a captured call reads its inputs when replayed: after the inputs are
+    # overwritten in place, a replay gives the eager result on the new values
+    q, k, v = (t.to(dev) for t in make_qkv(1, 2, 777, 128, "bf16", seed_base=36))
+    q2, k2, v2 = (t.to(dev) for t in make_qkv(1, 2, 777, 128, "bf16", seed_base=37))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, 777), dtype=torch.float32, device=dev)
+    call = lambda: iofa.fa_fwd(q, k, v, o, lse, default_scale(128))  # noqa: E731
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    o_ref, lse_ref = iofa.forward(q2, k2, v2)
+    for dst, src in ((q, q2), (k, k2), (v, v2)):
+        dst.copy_(src)
+    o.fill_(0)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.uint8), o_ref.view(torch.uint8))
+    assert torch.equal(lse, lse_ref)
