@@ -506,6 +506,13 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
                      dtype=torch.uint8, device=dev)
     flops = 4.0 * B * H * N * N * d
     f_ms = time_graph(lambda: iofa.fa_fwd(q, k, v, o, lse, scale), torch)
+    share = f"{spec['dtype']} B{B} H{H} N{N} d{d} (one GPU's share of an 8-way head split)"
+    if g == 1:
+        # too few key tiles per range for a split to pay: the call is fa_fwd
+        return {"workload": share, "num_splits": 1,
+                "timing": "20 calls captured in a graph, replayed 10 times between two events",
+                "fused_ms": round(f_ms, 4),
+                "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1)}
     s_ms = time_graph(lambda: iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, scale, g), torch)
     rows = B * H * N
     flat = ws.view(torch.float32)
@@ -516,7 +523,7 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     m_ms = time_graph(lambda: iofa.fa_merge_partials(o_part, lse_part, o2, l2), torch)
     merge_bytes = g * rows * (d + 1) * 4 + rows * (d * q.element_size() + 4)
     return {
-        "workload": f"{spec['dtype']} B{B} H{H} N{N} d{d} (one GPU's share of an 8-way head split)",
+        "workload": share,
         "num_splits": g,
         "timing": "20 calls captured in a graph, replayed 10 times between two events",
         "fused_ms": round(f_ms, 4), "fused_tflops": round(flops / (f_ms * 1e-3) / 1e12, 1),
