@@ -1,6 +1,6 @@
 // Naive three-kernel attention for gfx950: the standard-attention contrast
 // whose device-memory traffic section "MAC分析 / 标准Transformer MAC分析" of
-// the ctyun.cn FlashAttention article counts line by line:
+// the ctyun.cn FlashAttention article counts step by step:
 //   kernel 1: read Q, K; write S = scale * Q K^T        (2Nd + N^2 elements)
 //   kernel 2: read S; write P = softmax(S) row by row  (2N^2)
 //   kernel 3: read P, V; write O = P V                  (N^2 + 2Nd)
@@ -240,13 +240,25 @@ __global__ __launch_bounds__(256) void naive_softmax_f32(
 
 // ------------------------------------------------------- kernel 3 (16-bit)
 
+// O = P V for 128 query rows per workgroup (32 per wave), 64-key tiles.
+// Each lane holds one query row's P fragments (8 consecutive keys, straight
+// from global memory, the MFMA's B operand); V tiles are copied into LDS
+// with direct buffer loads (row-major, chunks swizzled as for the fused
+// kernel's V) and read back transposed with ds_read_b64_tr_b16 as the A
+// operand, so V needs neither staging registers nor transposing stores.
+// Iteration j issues the loads of tile j+1 (P into registers, V into the
+// other LDS stage) before multiplying tile j, and ends with a wait for them
+// and a barrier.
 template <class T, int D>
-__global__ __launch_bounds__(256) void naive_pv_16(
+__global__ __launch_bounds__(256, 4) void naive_pv_16(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int N, int ldS, int qtiles, int num_wg) {
-  constexpr int BC = 64, VS = BC + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int BC = 64;
+  constexpr uint32_t TB = BC * D * 2u;                 // bytes of one V stage
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * BC * D];
+  const uint32_t sm = lds_address(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int L = xcd_logical_id(blockIdx.x, num_wg);
   const int bh = L / qtiles, qt = L % qtiles;
@@ -254,12 +266,25 @@ __global__ __launch_bounds__(256) void naive_pv_16(
   const int q = qt * kQRows + wave * 32 + l32;
   const uint16_t* Prow = P + (static_cast<size_t>(bh) * N + q) * ldS;
 
-  f32x16 o[D / 32];
+  // V^T fragments: in each 16-lane group (g = lane / 16, t = lane % 16) lane
+  // t supplies row 8*(g/2) + t/4 and columns c0 + 4*(t%4) .. +3 and receives
+  // column c0 + t of 4 consecutive rows; the second read is 4 rows further.
+  // Lane half hi thus gets keys 16*ks + 8*hi + 0..7, the keys its P
+  // fragment holds.  The swizzle depends on row % 4 only.
+  uint32_t v_addr[D / 32];
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int row = 8 * (g >> 1) + (t >> 2);
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
+      const int chunk = (col >> 3) ^ v_swz<D>(row);
+      v_addr[cb] = sm + static_cast<uint32_t>(row * D + chunk * 8 + (col & 7)) * 2u;
+    }
+  }
+  TileCopy<D, BC, kSwzV> vcp;
+  vcp.init(wave, lane);
 
-  // P fragments and V rows of the next key tile are loaded while the
-  // current tile is multiplied
   using vec8 = typename T::vec8;
   auto load_p = [&](int k0, vec8 (&pf)[4]) {
 #pragma unroll
@@ -269,23 +294,34 @@ __global__ __launch_bounds__(256) void naive_pv_16(
                                      : __builtin_bit_cast(vec8, u32x4{0u, 0u, 0u, 0u});
     }
   };
-  VtTile<D, BC, VS> vt;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) o[cb] = f32x16{};
+  const int NT = (N + BC - 1) / BC;
   vec8 pcur[4], pnext[4];
-  vt.load(V + head, N, tid);
   load_p(0, pcur);
-  for (int k0 = 0; k0 < N; k0 += BC) {
-    vt.store(Vt, tid);
-    if (k0 + BC < N) {
-      vt.load(V + head + static_cast<size_t>(k0 + BC) * D, N - k0 - BC, tid);
-      load_p(k0 + BC, pnext);
+  vcp.copy(V + head, 0, N, sm);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < NT; ++j) {
+    const uint32_t cur = (j & 1) ? TB : 0u;
+    if (j + 1 < NT) {
+      load_p((j + 1) * BC, pnext);
+      vcp.copy(V + head, (j + 1) * BC, N, sm + (TB - cur));
     }
-    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-        o[cb] = T::mfma(lds_vec8<T>(Vt + (32 * cb + l32) * VS + 16 * ks + 8 * hi), pcur[ks], o[cb]);
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const uint32_t a0 = v_addr[cb] + cur + 16u * ks * D * 2u;
+        const s16x4 lo = lds_read_tr8(a0);
+        const s16x4 up = lds_read_tr8(a0 + 4u * D * 2u);
+        const auto a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[cb] = T::mfma(a, pcur[ks], o[cb]);
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pcur[ks] = pnext[ks];
