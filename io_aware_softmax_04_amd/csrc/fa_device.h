@@ -99,84 +99,6 @@ __device__ inline int xcd_logical_id(int w, int G) {
 
 // ------------------------------------------------------------ tile loads
 
-// K (or Q) tile of BC rows x D 16-bit elements into LDS rows of stride KS
-// elements.  Rows at or beyond `rows_valid` are filled with zeros.  256
-// threads; each owns KCH 16-byte chunks; consecutive threads read consecutive
-// chunks of one row (coalesced).
-template <int D, int BC, int KS>
-struct RowTile {
-  static constexpr int CH = D / 8;
-  static constexpr int KCH = BC * CH / 256;
-  static_assert(KCH * 256 == BC * CH, "tile must split into 256 threads");
-  u32x4 r[KCH];
-
-  __device__ inline void load(const uint16_t* __restrict__ base, int rows_valid,
-                              int tid) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / CH, cc = c % CH;
-      if (row < rows_valid)
-        r[i] = *reinterpret_cast<const u32x4*>(base + row * D + cc * 8);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ inline void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / CH, cc = c % CH;
-      *reinterpret_cast<u32x4*>(lds + row * KS + cc * 8) = r[i];
-    }
-  }
-};
-
-// V tile of BC keys x D 16-bit elements, stored transposed in LDS as D rows
-// of stride VS elements (one row per output column c, keys along the row).
-// Each thread loads KPB consecutive keys of one 16-byte column chunk and
-// writes, for each of its 8 columns, KPB keys (in natural order) as one
-// KPB*2-byte store.  Keys at or beyond `rows_valid` are zeros.
-template <int D, int BC, int VS>
-struct VtTile {
-  static constexpr int CH = D / 8;
-  static constexpr int KPB = BC * CH / 256;
-  static constexpr int NKG = BC / KPB;
-  static_assert(KPB == 1 || KPB == 2 || KPB == 4, "unsupported V tile shape");
-  u32x4 r[KPB];
-
-  __device__ inline void load(const uint16_t* __restrict__ base, int rows_valid,
-                              int tid) {
-    const int kg = tid % NKG, cc = tid / NKG;
-#pragma unroll
-    for (int i = 0; i < KPB; ++i) {
-      const int key = kg * KPB + i;
-      if (key < rows_valid)
-        r[i] = *reinterpret_cast<const u32x4*>(base + key * D + cc * 8);
-      else
-        r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ inline void store(uint16_t* lds, int tid) const {
-    const int kg = tid % NKG, cc = tid / NKG;
-    const int pos = kg * KPB;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = lds + (cc * 8 + e) * VS + pos;
-      if constexpr (KPB == 4) {
-        u32x2 w;
-        w[0] = half_of(r[0], e) | (half_of(r[1], e) << 16);
-        w[1] = half_of(r[2], e) | (half_of(r[3], e) << 16);
-        *reinterpret_cast<u32x2*>(dst) = w;
-      } else if constexpr (KPB == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = half_of(r[0], e) | (half_of(r[1], e) << 16);
-      } else {
-        *dst = static_cast<uint16_t>(half_of(r[0], e));
-      }
-    }
-  }
-};
-
 // ------------------------------------------- swizzled LDS tiles (fused path)
 //
 // K and V tiles of BC rows x D 16-bit elements are copied from global memory

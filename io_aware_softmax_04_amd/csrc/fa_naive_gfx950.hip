@@ -20,6 +20,41 @@ constexpr int kQRows = 128;        // query rows per workgroup (4 waves x 32)
 constexpr int kKeysPerWg = 256;    // keys per workgroup in kernel 1
 constexpr int kMaxChunks = 16;     // 8-element chunks per thread in kernel 2 (N <= 32768)
 
+// K tile of BC rows x D 16-bit elements into LDS rows of stride KS elements
+// (kernel 1).  256 threads; each owns KCH 16-byte chunks; consecutive threads
+// read consecutive chunks of one row (coalesced).  The loads are range-checked
+// buffer loads over the tile's valid rows, so rows at or beyond `rows_valid`
+// arrive as zeros without a branch, and the compiler can count them exactly
+// in its waits.
+template <int D, int BC, int KS>
+struct RowTile {
+  static constexpr int CH = D / 8;
+  static constexpr int KCH = BC * CH / 256;
+  static_assert(KCH * 256 == BC * CH, "tile must split into 256 threads");
+  u32x4 r[KCH];
+
+  __device__ inline void load(const uint16_t* __restrict__ base, int rows_valid, int tid) {
+    // workgroup-uniform: keeps the buffer descriptor in scalar registers
+    const int rows = __builtin_amdgcn_readfirstlane(rows_valid > 0 ? (rows_valid < BC ? rows_valid : BC) : 0);
+    const auto rsrc = buffer_rsrc(base, static_cast<uint32_t>(rows) * (D * 2u));
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / CH, cc = c % CH;
+      r[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (row * D + cc * 8) * 2, 0, 0));
+    }
+  }
+  __device__ inline void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / CH, cc = c % CH;
+      *reinterpret_cast<u32x4*>(lds + row * KS + cc * 8) = r[i];
+    }
+  }
+};
+
 // ------------------------------------------------ element access (kernel 2)
 
 struct Ld16Bf16 {
@@ -68,7 +103,7 @@ __device__ inline float block_reduce(float x, bool is_max, float* red) {
 // ------------------------------------------------------- kernel 1 (16-bit)
 
 template <class T, int D>
-__global__ __launch_bounds__(256) void naive_scores_16(
+__global__ __launch_bounds__(256, 4) void naive_scores_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     uint16_t* __restrict__ S, int N, int ldS, int qtiles, int ktiles, int num_wg,
     float scale) {
@@ -89,13 +124,23 @@ __global__ __launch_bounds__(256) void naive_scores_16(
   for (int kk = 0; kk < D / 16; ++kk)
     qf[kk] = (q < N) ? gmem_vec8<T>(Q + head + static_cast<size_t>(q) * D + 16 * kk + 8 * hi)
                      : __builtin_bit_cast(typename T::vec8, u32x4{0u, 0u, 0u, 0u});
+  // The K rows of the next 64-key block are loaded while this block is
+  // multiplied and its scores are stored, so the wait for them (which on
+  // this GPU also waits for every store issued before them) never waits for
+  // the current block's stores.
+  RowTile<D, BC, KS> t;
+  {
+    const int k0 = kt * kKeysPerWg;
+    t.load(K + head + static_cast<size_t>(k0) * D, N - k0, tid);
+  }
+#pragma unroll
   for (int sub = 0; sub < kKeysPerWg / BC; ++sub) {
     const int k0 = kt * kKeysPerWg + sub * BC;
     if (k0 >= N) break;
-    RowTile<D, BC, KS> t;
-    t.load(K + head + static_cast<size_t>(k0) * D, N - k0, tid);
     t.store(Ks, tid);
     __syncthreads();
+    const int k1 = k0 + BC;
+    if (sub + 1 < kKeysPerWg / BC) t.load(K + head + static_cast<size_t>(k1) * D, N - k1, tid);
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
@@ -115,16 +160,25 @@ __global__ __launch_bounds__(256) void naive_scores_16(
       }
     __syncthreads();
     constexpr int CPR = BC / 8;                         // 16-byte pieces per row
+    // Range-checked buffer stores over the workgroup's valid rows of S: a
+    // piece outside them (a row at or beyond N, or a key at or beyond ldS)
+    // gets an offset past the range and is dropped.  Being branch-free, the
+    // stores are counted exactly by the compiler's waits, so the next
+    // block's K loads (issued before them) are waited for without them.
+    // ldS is a multiple of 8, so a piece that starts before ldS ends there at
+    // the latest; columns in [N, ldS) are never read as scores.
+    const int qrows = N - qt * kQRows < kQRows ? N - qt * kQRows : kQRows;
+    const uint32_t sbytes = static_cast<uint32_t>(qrows) * static_cast<uint32_t>(ldS) * 2u;
+    const auto srsrc = buffer_rsrc(S + (static_cast<size_t>(bh) * N + qt * kQRows) * ldS, sbytes);
 #pragma unroll
     for (int i = 0; i < kQRows * CPR / 256; ++i) {
       const int c = tid + 256 * i;
       const int r = c / CPR, key = k0 + 8 * (c % CPR);
-      const int qr = qt * kQRows + r;
-      // ldS is a multiple of 8, so a piece that starts before ldS ends there
-      // at the latest; columns in [N, ldS) are never read as scores
-      if (qr < N && key < ldS)
-        *reinterpret_cast<u32x4*>(S + (static_cast<size_t>(bh) * N + qr) * ldS + key) =
-            *reinterpret_cast<const u32x4*>(Ss + r * SS + 8 * (c % CPR));
+      const uint32_t off = (r < qrows && key < ldS)
+                               ? (static_cast<uint32_t>(r) * ldS + key) * 2u : sbytes;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          *reinterpret_cast<const u32x4*>(Ss + r * SS + 8 * (c % CPR)),
+          srsrc, static_cast<int>(off), 0, 0);
     }
     __syncthreads();
   }
