@@ -239,6 +239,35 @@ def test_naive_without_lse(dev):
     assert max_abs <= 2e-2 and rel_f <= 1e-2
 
 
+@pytest.mark.parametrize("dtype,N,d", [("bf16", 1000, 128), ("fp16", 65, 64), ("fp32", 100, 128)])
+def test_naive_no_writes_outside_outputs(dtype, N, d, dev):
+    # O, LSE and both workspaces sit inside guard regions that must come back
+    # unchanged (the scores kernel drops pieces of S outside the valid rows
+    # and keys through range-checked stores; the other kernels bound their
+    # writes by index)
+    B, H = 1, 2
+    q, k, v = (t.to(dev) for t in make_qkv(B, H, N, d, dtype, seed_base=7 * N + d))
+    guard = 4096
+    nb = iofa.fa_naive_workspace_bytes(B, H, N, q.dtype)
+    s_buf = torch.full((guard + nb + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    p_buf = torch.full((guard + nb + guard,), 0x5A, dtype=torch.uint8, device=dev)
+    n = B * H * N * d
+    o_buf = torch.full((guard + n + guard,), float("nan"), dtype=q.dtype, device=dev)
+    l_buf = torch.full((guard + B * H * N + guard,), float("nan"), dtype=torch.float32, device=dev)
+    o = o_buf[guard:guard + n].view(B, H, N, d)
+    lse = l_buf[guard:guard + B * H * N].view(B, H, N)
+    iofa.fa_naive_fwd(q, k, v, o, lse, s_buf[guard:guard + nb], p_buf[guard:guard + nb],
+                      default_scale(d))
+    torch.cuda.synchronize()
+    for buf, fill in ((s_buf, 0xA5), (p_buf, 0x5A)):
+        assert bool((buf[:guard] == fill).all()) and bool((buf[guard + nb:] == fill).all())
+    for buf, size in ((o_buf, n), (l_buf, B * H * N)):
+        assert bool(torch.isnan(buf[:guard]).all()) and bool(torch.isnan(buf[guard + size:]).all())
+    o_ref, lse_ref = oracle_full(q.cpu(), k.cpu(), v.cpu(), default_scale(d))
+    max_abs, rel_f, _ = errors(o.cpu(), lse.cpu(), o_ref, lse_ref)
+    assert max_abs <= 2e-2 and rel_f <= 1e-2
+
+
 def test_inputs_may_share_one_buffer(dev):
     # self-attention on one tensor: Q, K and V are the same device buffer
     x, _, _ = make_qkv(1, 2, 333, 128, "bf16", seed_base=95)
