@@ -15,7 +15,9 @@ LSE_g = m_g + ln l_g; then, for every query row,
     O   = sum_g e^{LSE_g - LSE} O_g
 
 because e^{LSE_g - LSE} = e^{m_g - m} l_g / l = l(p_g)^global / l(x).  A block
-with no keys has LSE_g = -inf and O_g = 0, and contributes nothing.
+with no keys has LSE_g = -inf and O_g = 0, and contributes nothing; a row all
+of whose blocks are empty therefore sums no terms: LSE = ln 0 = -inf and
+O = 0.
 
 ``partial_attention`` is the plain definition restricted to a key range; it
 uses the same per-head steps as ``standard_attention``.  ``merge_partials`` is the
@@ -62,7 +64,8 @@ def merge_partials(o_parts, lse_parts):
     safe = np.where(np.isfinite(ref), ref, 0.0)
     w = np.exp(lse_parts - safe)                         # e^{LSE_g - ref}, 0 for -inf
     total = w.sum(axis=0)
-    lse = safe + np.log(total)
-    weights = w / total
+    with np.errstate(divide="ignore"):
+        lse = safe + np.log(total)                       # -inf where every block is empty
+    weights = np.divide(w, total, out=np.zeros_like(w), where=total > 0)
     o = (weights[..., None] * o_parts).sum(axis=0)
     return o, lse

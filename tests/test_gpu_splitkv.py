@@ -110,6 +110,7 @@ def test_merge_entry_point(out_dtype, d, dev):
         lse_part = rng.uniform(-20, 20, (G, rows)).astype(np.float32)
         if G > 1:
             lse_part[0, ::3] = -np.inf            # blocks without keys
+            lse_part[:, 1::7] = -np.inf           # rows whose blocks are all empty
         o_ref, lse_ref = oracle.merge_partials(o_part.astype(np.float64),
                                                lse_part.astype(np.float64))
         o = torch.empty(rows, d, dtype=out_dtype, device=dev)
@@ -122,4 +123,9 @@ def test_merge_entry_point(out_dtype, d, dev):
         # output rounding u|O| plus fp32 arithmetic over G terms
         bound = u[out_dtype] * np.abs(o_ref) + 1e-5 * (1 + np.abs(o_ref))
         assert np.all(np.abs(got - o_ref) <= bound), (G, rows, np.abs(got - o_ref).max())
-        assert np.abs(lse.cpu().double().numpy() - lse_ref).max() <= 1e-5 * (1 + np.abs(lse_ref).max())
+        got_lse = lse.cpu().double().numpy()
+        empty = np.isneginf(lse_ref)
+        assert np.array_equal(np.isneginf(got_lse), empty)
+        assert np.all(got[empty] == 0)
+        fin = ~empty
+        assert np.abs(got_lse[fin] - lse_ref[fin]).max() <= 1e-5 * (1 + np.abs(lse_ref[fin]).max())

@@ -465,6 +465,24 @@ def test_merge_identities():
         assert np.abs(other[1] - ab[1]).max() <= 1e-14
 
 
+def test_merge_of_rows_without_keys():
+    # rows whose blocks are all empty sum no terms (O = 0, LSE = -inf); the
+    # other rows are unaffected by an empty block next to them
+    q, k, v = _random_head(6)
+    a = oracle.partial_attention(q, k, v, 0.5, 0, 37)
+    empty = oracle.partial_attention(q, k, v, 0.5, 9, 9)
+    o, lse = oracle.merge_partials(np.stack([empty[0], empty[0]]), np.stack([empty[1], empty[1]]))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    o_parts = np.stack([a[0], empty[0]])
+    lse_parts = np.stack([a[1], empty[1]])
+    lse_parts[0, 0, 0, ::2] = -np.inf               # every other row: both blocks empty
+    o_parts[0, 0, 0, ::2] = 0.0
+    o, lse = oracle.merge_partials(o_parts, lse_parts)
+    assert np.all(o[0, 0, ::2] == 0) and np.all(lse[0, 0, ::2] == -np.inf)
+    assert np.abs(o[0, 0, 1::2] - a[0][0, 0, 1::2]).max() <= 1e-15
+    assert np.abs(lse[0, 0, 1::2] - a[1][0, 0, 1::2]).max() <= 1e-15
+
+
 @pytest.mark.parametrize("n", [2, 5, 16])
 def test_merge_weights_match_two_block_softmax(n):
     # one query row, V = identity: the output row is the attention weights, so
