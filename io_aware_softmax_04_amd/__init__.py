@@ -105,12 +105,25 @@ def load_library():
 
 # ----------------------------------------------------------- marshalling
 
+def _device_address(t):
+    # Every pointer handed to the library is device memory of the current
+    # device (the entry points run under torch.cuda.device of their first
+    # tensor): a host tensor or one on another GPU would reach the kernels
+    # as an address they cannot use, so it is rejected here.
+    if not t.is_cuda:
+        raise ValueError(f"tensors must be on a GPU; got one on {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors must all be on one GPU; got cuda:{t.device.index} "
+                         f"alongside cuda:{torch.cuda.current_device()}")
+    return t.data_ptr()
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else ctypes.c_void_p(_device_address(t))
 
 
 def _fptr(t):
-    return None if t is None else ctypes.cast(ctypes.c_void_p(t.data_ptr()),
+    return None if t is None else ctypes.cast(ctypes.c_void_p(_device_address(t)),
                                               ctypes.POINTER(ctypes.c_float))
 
 

@@ -316,3 +316,14 @@ def test_fp8_extents_are_one_byte_inputs_and_bf16_output(lib):
 
 def test_fp8_empty_problem(lib):
     assert fp8(lib, q=0, k=0, v=0, o=0, lse=0, N=0) == 0
+
+
+def test_binding_refuses_host_tensors():
+    # host tensors never reach the library (their addresses are not device
+    # memory); the call raises before any pointer is passed
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        iofa.fa_fwd(q, q, q, torch.empty_like(q), torch.empty(1, 1, 8), 0.125)
+    with pytest.raises(ValueError):
+        iofa.softmax(torch.zeros(2, 10))

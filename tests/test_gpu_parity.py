@@ -180,6 +180,25 @@ def test_errors_surface_through_binding(dev):
     assert ei.value.status == 3
 
 
+def test_host_tensors_are_rejected_before_the_library(dev):
+    # a host pointer would reach the kernels as an unusable address: the
+    # binding refuses it (output, statistics or workspace alike)
+    q, k, v = (t.to(dev) for t in make_qkv(1, 1, 64, 128, "bf16", seed_base=2))
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 1, 64, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError, match="on a GPU"):
+        iofa.fa_fwd(q, k, v, o, torch.empty(1, 1, 64), 0.1)
+    with pytest.raises(ValueError):
+        iofa.fa_fwd(q, k, v, o.cpu(), lse, 0.1)
+    ws = torch.empty(iofa.fa_splitkv_workspace_bytes(1, 1, 64, 128, q.dtype, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="on a GPU"):
+        iofa.fa_fwd_splitkv(q, k, v, o, lse, ws, 0.1, 2)
+    x = torch.zeros(2, 100, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="on a GPU"):
+        iofa.fa_softmax_rows(x, torch.empty(2, 100, dtype=torch.bfloat16), None)
+    torch.cuda.synchronize()
+
+
 # ----------------------------------------------------------- naive path
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 5])
