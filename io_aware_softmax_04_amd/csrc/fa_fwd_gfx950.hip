@@ -70,7 +70,9 @@ struct WaveState {
   vec8 qf[D / 16];               // Q fragments (B operand of S^T = K Q^T)
   f32x16 o[D / 32];              // O^T accumulator: lane owns one query column
   float m_run;                   // reference maximum, log2 units of scaled scores
-  float l_run;                   // denominator relative to m_run
+  float l_run;                   // this lane half's share of the denominator (the
+                                 // keys it holds), relative to m_run; the two
+                                 // halves are added in the epilogue
   int hi;                        // lane half (0: lanes 0-31, 1: lanes 32-63)
   uint32_t k_addr[D / 16];       // LDS byte address of the K fragment, stage 0
   uint32_t v_addr[D / 32];       // LDS byte address of the V^T read, stage 0
@@ -182,7 +184,6 @@ struct WaveState {
       for (int e = 0; e < 4; ++e) w[e] = T::pack(p[b + 2 * e], p[b + 2 * e + 1]);
       pk[ks] = __builtin_bit_cast(vec8, w);
     }
-    rs = halfwave_sum(rs);
     l_run = alpha * l_run + rs;
     return alpha;
   }
@@ -222,15 +223,16 @@ struct WaveState {
     }
     return rs;
   }
-  // Accept a lazy tile (returns 1) or redo it with its maximum (returns the
-  // rescale factor of the older terms).
-  __device__ inline float commit_lazy(float rs, f32x16 (&s)[C::SB], vec8 (&pk)[C::KSTEPS],
-                                      float c2) {
+  // Accept a lazy tile (returns false) or redo it with its maximum (returns
+  // true, with the rescale factor of the older terms in alpha).
+  __device__ inline bool commit_lazy(float rs, f32x16 (&s)[C::SB], vec8 (&pk)[C::KSTEPS],
+                                     float c2, float& alpha) {
     if (__all(rs <= kLazyBound<T>)) {
-      l_run += halfwave_sum(rs);
-      return 1.f;
+      l_run += rs;
+      return false;
     }
-    return softmax<false>(s, pk, c2, BC);
+    alpha = softmax<false>(s, pk, c2, BC);
+    return true;
   }
 
   __device__ inline void rescale(float alpha) {
@@ -341,7 +343,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     ws.template pv<1 - P>(p_prev);
     ws.template scores<1 - P>(s_nxt);
     interleave_mfma_valu<NM, NRD, LEAD, 4>();
-    bottom(ws.commit_lazy(rs, s_cur, p_cur, c2));
+    // the redo decision is wave-uniform, so the accepted path (almost every
+    // tile) carries no rescale factor and no rescale test
+    float alpha;
+    if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
   // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
@@ -388,8 +395,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   // LSE = ln2 * (m + log2 l).  Lane half hi holds columns 32*cb + 8*g + 4*hi
   // + 0..3 in registers 4*g .. 4*g+3.
   if (q < N) {
-    const float inv_l = 1.0f / ws.l_run;
-    const float lse = (ws.m_run + __builtin_amdgcn_logf(ws.l_run)) * kLn2;
+    const float l = halfwave_sum(ws.l_run);
+    const float inv_l = 1.0f / l;
+    const float lse = (ws.m_run + __builtin_amdgcn_logf(l)) * kLn2;
     if constexpr (PARTIAL) {
       const size_t row = (static_cast<size_t>(gp.split) * BH + bh) * N + q;
       float* Oq = static_cast<float*>(Out) + row * D;
