@@ -438,7 +438,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         const int r = 4 * g + i;
         const int qi = 8 * g + 4 * hi + i;
         float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[i]));
-        pr = qi < qvalid ? pr : 0.f;
+        // Query rows at or beyond N need no mask: their Q and dO rows and
+        // their statistics arrive as zeros, so P = 1 there meets dO = 0 in
+        // dV and dS = 1 * (0 - 0) = 0 in dK -- exact zeros either way.  At
+        // d = 128 dropping the select saves 16 VALU instructions per tile
+        // (2% of the backward); at d = 64 the select-free instance measured
+        // slower on short sequences, so it keeps the mask.
+        if (D == 64) pr = qi < qvalid ? pr : 0.f;
         p[r] = pr;
         dsv[r] = pr * (dp[r] - dd[i]);
       }
