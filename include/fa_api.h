@@ -254,7 +254,8 @@ size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype);
  *   dQ, dK, dV      out: (B, H, N, d) `dtype`, 16-byte aligned, overlapping
  *                        no input, each other or the workspace.
  *   workspace       caller-owned, fa_bwd_workspace_bytes(B, H, N) bytes,
- *                   16-byte aligned; holds (LSE * log2 e, D) per row on return.
+ *                   16-byte aligned; holds (LSE * log2 e, -D) per row on return,
+ *                   D = rowsum(dO * O).
  * Other arguments and errors as fa_fwd.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

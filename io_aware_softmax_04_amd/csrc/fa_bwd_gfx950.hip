@@ -9,7 +9,7 @@
 //     dV = P^T dO,   dQ = scale * dS K,   dK = scale * dS^T Q.
 //
 // Three kernels:
-//   bwd_stats    per row: (L * log2 e, D) into an fp32 pair workspace;
+//   bwd_stats    per row: (L * log2 e, -D) into an fp32 pair workspace;
 //   bwd_dq       one workgroup per 128 query rows (4 waves x 32), K and V
 //                tiles of 32 keys streamed through LDS; per tile
 //                S^T = K Q^T, dP^T = V dO^T (both v_mfma_f32_32x32x16 with
@@ -48,8 +48,9 @@ constexpr int kBwdRows = 128;                // rows a workgroup owns (4 waves x
 
 // ------------------------------------------------------------- stats pass
 
-// (L[r] * log2 e, D[r]) for every row r of B*H*N.  D/8 threads per row, each
-// 8 columns (16-byte loads).
+// (L[r] * log2 e, -D[r]) for every row r of B*H*N.  D/8 threads per row, each
+// 8 columns (16-byte loads).  D enters dS = P (dP - D) negated, so the dK/dV
+// kernel can start its dP accumulator from it.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restrict__ O,
                                                         const uint16_t* __restrict__ dO,
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const uint16_t* __restri
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (r < rows && c8 == 0) stats[r] = make_float2(LSE[r] * kLog2e, acc);
+  if (r < rows && c8 == 0) stats[r] = make_float2(LSE[r] * kLog2e, -acc);
 }
 
 // ------------------------------------------------------------ shared steps
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   load_row_frags<T, D>(qf, Q + head + static_cast<size_t>(q) * D, qv, hi);
   load_row_frags<T, D>(df, dO + head + static_cast<size_t>(q) * D, qv, hi);
   const float2 st = qv ? stats[static_cast<size_t>(bh) * N + q] : make_float2(0.f, 0.f);
-  const float lse2 = st.x, Dq = st.y;
+  const float lse2 = st.x, negD = st.y;
   const float c2 = scale * kLog2e;
   f32x16 acc[D / 32];
 #pragma unroll
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
         p = key < kvalid ? p : 0.f;
       }
-      ds[r] = p * (dp_[SET][r] - Dq);
+      ds[r] = p * (dp_[SET][r] + negD);
     }
     pack_b<T>(ds, pk_[SET]);
   };
@@ -385,11 +386,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   // offsets of a 32-row tile serve them
   const uint32_t vwave = vbase + static_cast<uint32_t>(wave) * 32u * D * 2u;
   const float2* sh = stats + static_cast<size_t>(bh) * N;
+  // the tile's 32 (lse2, -D) pairs, split on the way into LDS: lanes 0..31
+  // copy the lse2 of rows 0..31, lanes 32..63 their -D, so the stage holds
+  // an lse2 plane then a -D plane (128 bytes each)
+  const uint32_t stats_voff = static_cast<uint32_t>(lane & 31) * 8u + static_cast<uint32_t>(hi) * 4u;
   auto stats_copy = [&](int q0, uint32_t dst) {
     if (wave == 0) {
       const int rows = N - q0 > 0 ? N - q0 : 0;
       const auto rsrc = buffer_rsrc(sh + q0, static_cast<uint32_t>(rows) * 8u);
-      lds_dma4(rsrc, static_cast<uint32_t>(lane) * 4u, dst);
+      lds_dma4(rsrc, stats_voff, dst);
     }
   };
   const int NT = (N + BQ - 1) / BQ;
@@ -419,25 +424,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
       stats_copy((j + 1) * BQ, sm + 4 * TB + (1 - P) * SB);
     }
     const uint32_t qs = sm + P * TB, dos = sm + (2 + P) * TB, ss = sm + 4 * TB + P * SB;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // this lane's 16 query rows: 8*g + 4*hi + 0..3 for g = 0..3, register
+    // 4*g + i of both accumulators.  dP starts from -D of its row, so the
+    // accumulator ends as dP - D and dS = P * (dP - D) takes one multiply.
+    f32x16 s = f32x16{}, dp;
+    u32x4 l2w[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t a = ss + static_cast<uint32_t>(8 * g + 4 * hi) * 4u;
+      l2w[g] = lds_read16(a);
+      const u32x4 nd = lds_read16(a + 128u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dp[4 * g + i] = __uint_as_float(nd[i]);
+    }
     rows_times<T, D>(s, qs, lo, kf);         // S  (queries x keys)
-    rows_times_lds<T, D>(dp, dos, vwave, lo);  // dP
-    // this lane's 16 query rows: 8*g + 4*hi + 0..3 for g = 0..3
+    rows_times_lds<T, D>(dp, dos, vwave, lo);  // dP - D
     const int qvalid = N - j * BQ;
     f32x16 p, dsv;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t a = ss + static_cast<uint32_t>(8 * g + 4 * hi) * 8u;
-      const u32x4 s01 = lds_read16(a), s23 = lds_read16(a + 16);   // (lse2, D) x 4
-      const float l2[4] = {__uint_as_float(s01[0]), __uint_as_float(s01[2]),
-                           __uint_as_float(s23[0]), __uint_as_float(s23[2])};
-      const float dd[4] = {__uint_as_float(s01[1]), __uint_as_float(s01[3]),
-                           __uint_as_float(s23[1]), __uint_as_float(s23[3])};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
         const int qi = 8 * g + 4 * hi + i;
-        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l2[i]));
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -__uint_as_float(l2w[g][i])));
         // Query rows at or beyond N need no mask: their Q and dO rows and
         // their statistics arrive as zeros, so P = 1 there meets dO = 0 in
         // dV and dS = 1 * (0 - 0) = 0 in dK -- exact zeros either way.  At
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         // slower on short sequences, so it keeps the mask.
         if (D == 64) pr = qi < qvalid ? pr : 0.f;
         p[r] = pr;
-        dsv[r] = pr * (dp[r] - dd[i]);
+        dsv[r] = pr * dp[r];
       }
     }
     vec8 pp[2], pd[2];
