@@ -241,6 +241,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   load_row_frags<T, D>(df, dO + head + static_cast<size_t>(q) * D, qv, hi);
   const float2 st = qv ? stats[static_cast<size_t>(bh) * N + q] : make_float2(0.f, 0.f);
   const float lse2 = st.x, negD = st.y;
+  // dP^T starts from -D (the lane's query), so it ends as dP - D and dS is one
+  // multiply per element; the first dP product reads this block as its
+  // accumulator input, so the start costs no vector instruction per tile
+  f32x16 nd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd16[r] = negD;
   const float c2 = scale * kLog2e;
   f32x16 acc[D / 32];
 #pragma unroll
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   auto scores = [&](auto set, auto ks, auto vs) {
     constexpr int SET = decltype(set)::value, KS = decltype(ks)::value, VS = decltype(vs)::value;
     s_[SET] = f32x16{};
-    dp_[SET] = f32x16{};
+    dp_[SET] = nd16;
     rows_times<T, D>(s_[SET], sm + KS * TB, lo, qf);          // S^T  (keys x queries)
     rows_times<T, D>(dp_[SET], sm + (4 + VS) * TB, lo, df);   // dP^T
   };
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
         p = key < kvalid ? p : 0.f;
       }
-      ds[r] = p * (dp_[SET][r] + negD);
+      ds[r] = p * dp_[SET][r];
     }
     pack_b<T>(ds, pk_[SET]);
   };
