@@ -303,12 +303,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     constexpr int J = decltype(jm)::value;
     using Cur = std::integral_constant<int, J % 2>;
     using Nxt = std::integral_constant<int, (J + 1) % 2>;
+    // raised issue priority through the products, dropped before the
+    // barrier, as in the forward kernels
+    __builtin_amdgcn_s_setprio(1);
     if (j + 2 < NT) copy_tile(j + 2);
     softmax_ds(Cur{}, NoTail{}, BC);
     dq_update(Nxt{}, std::integral_constant<int, (J + 3) % 4>{});    // tile j-1
     scores(Nxt{}, std::integral_constant<int, (J + 1) % 4>{},
            std::integral_constant<int, (J + 1) % 2>{});             // tile j+1
     interleave_mfma_valu<NM, NRD, 8, 3>();
+    __builtin_amdgcn_s_setprio(0);
     bottom();
   };
   // last iteration j = NT-1 (> 0), J = j % 4: no copies, no scores
@@ -424,6 +428,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     constexpr int P = decltype(par)::value;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);   // dropped again at the tile's end
     if (j + 1 < NT) {
       qcp.copy(Q + head, (j + 1) * BQ, N, sm + (1 - P) * TB);
       dcp.copy(dO + head, (j + 1) * BQ, N, sm + (3 - P) * TB);
@@ -470,6 +475,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     pack_b<T>(dsv, pd);
     cols_times<T, D>(dv, dos, lo, pp);       // dV^T += dO^T P
     cols_times<T, D>(dk, qs, lo, pd);        // dK^T += Q^T dS
+    __builtin_amdgcn_s_setprio(0);
   };
   int j = 0;
   for (; j + 1 < NT; j += 2) {

@@ -371,6 +371,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(
   auto iteration = [&](auto par, int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], i32x8& p_prev,
                        i32x8& p_cur) {
     constexpr int P = decltype(par)::value;
+    // raised issue priority from the copies through the products, dropped
+    // before the wait and barrier (measured 1-4% faster, same output)
+    __builtin_amdgcn_s_setprio(1);
     kcp.copy(Kh, (j + 2) * C::BC, N, kst[P]);
     vcp.copy(Vh, j * C::BC, N, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
@@ -381,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(
     // tile) carries no rescale factor and no rescale test
     float alpha;
     if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };

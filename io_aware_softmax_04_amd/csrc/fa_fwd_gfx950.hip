@@ -337,6 +337,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
                        vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
     constexpr int P = decltype(par)::value;
+    // raised issue priority from the copies through the products; dropped
+    // again before the wait and barrier (measured 0.8% faster at d = 128,
+    // 3.8% at d = 64, bit-identical output)
+    __builtin_amdgcn_s_setprio(1);
     kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
     vcp.copy(Vh, j * BC, NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     // tile) carries no rescale factor and no rescale test
     float alpha;
     if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
