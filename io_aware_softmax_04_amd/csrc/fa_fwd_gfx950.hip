@@ -137,6 +137,34 @@ struct WaveState {
     }
   }
 
+  // a6 of the previous tile and a3 of the next, their products alternating
+  // (score product i, then P V product i) so each K fragment read has
+  // several products of lead time instead of one.
+  template <int SV, int SK>
+  __device__ inline void pv_scores(const vec8 (&pk)[C::KSTEPS], f32x16 (&s)[C::SB]) {
+    constexpr int NS = (D / 16) * C::SB;
+    constexpr int NP = C::KSTEPS * (D / 32);
+    constexpr int NI = NS > NP ? NS : NP;
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) s[sb] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i < NS) {
+        const int kk = i / C::SB, sb = i % C::SB;
+        const auto a = __builtin_bit_cast(vec8, lds_read16(k_addr[kk] + SK * C::TB + 32 * sb * D * 2));
+        s[sb] = T::mfma(a, qf[kk], s[sb]);
+      }
+      if (i < NP) {
+        const int ks = i / (D / 32), cb = i % (D / 32);
+        const uint32_t a0 = v_addr[cb] + SV * C::TB + 16 * ks * D * 2;
+        const s16x4 lo = lds_read_tr8(a0);
+        const s16x4 up = lds_read_tr8(a0 + 8 * D * 2);
+        const auto a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[cb] = T::mfma(a, pk[ks], o[cb]);
+      }
+    }
+  }
+
   // a4 + a5: tile maximum, reference-maximum update, exponentials, row sum,
   // packing of P to the input type.  Returns the rescale factor of the older
   // terms.  TAIL masks keys at or beyond keys_valid to weight 0.
@@ -325,9 +353,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
 
   constexpr int NM = 2 * (D / 16) * C::SB;          // products per iteration
   constexpr int NRD = (D / 16) * C::SB + 2 * NM / 2;  // K reads + 2 per P V product
-  // LDS reads issued ahead of the interleaved products (measured: 10 at
-  // d = 128 and 16 at d = 64 were fastest without spills)
-  constexpr int LEAD = D == 128 ? 10 : 16;
+  // LDS reads issued ahead of the interleaved products (measured with the
+  // score and P V products alternating: 6 at d = 128 and 8 at d = 64)
+  constexpr int LEAD = D == 128 ? 6 : 8;
   auto bottom = [&](float alpha) {
     ws.rescale(alpha);
     __builtin_amdgcn_s_waitcnt(0);
@@ -344,8 +372,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
     vcp.copy(Vh, j * BC, NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
-    ws.template pv<1 - P>(p_prev);
-    ws.template scores<1 - P>(s_nxt);
+    ws.template pv_scores<1 - P, 1 - P>(p_prev, s_nxt);
     interleave_mfma_valu<NM, NRD, LEAD, 4>();
     // the redo decision is wave-uniform, so the accepted path (almost every
     // tile) carries no rescale factor and no rescale test
