@@ -241,6 +241,15 @@ def summarise_trace(trace_dir, index, spec, bench_args):
             groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     flops = 4.0 * spec["B"] * spec["H"] * spec["N"] ** 2 * spec["d"]
     tag = workload_tag(spec)
+    # the profiled run's own JSON line, when its stdout was kept beside the trace
+    bench_line = None
+    out_path = os.path.join(trace_dir, BENCH_STDOUT)
+    if os.path.exists(out_path):
+        with open(out_path, encoding="utf-8") as fh:
+            rows = [ln for ln in fh if ln.startswith("{")]
+        if rows:
+            bench_line = json.loads(rows[-1])
+    redirect = f" > {out_path}" if bench_line is not None else ""
     lines = [
         f"# Kernel trace, {spec['name']}",
         "",
@@ -248,7 +257,7 @@ def summarise_trace(trace_dir, index, spec, bench_args):
         "",
         "```",
         f"rocprofv3 --kernel-trace --stats -d {trace_dir} -o run --output-format csv -- "
-        f"python bench.py {bench_args}",
+        f"python bench.py {bench_args}{redirect}",
         f"python bench.py --workload {index} --trace-from {trace_dir} --trace-cmd='{bench_args}'",
         "```",
         "",
@@ -259,6 +268,7 @@ def summarise_trace(trace_dir, index, spec, bench_args):
         "| kernel | grid | calls | average (ns) | min (ns) | max (ns) | TFLOP/s at 4BHN^2d |",
         "|---|---|---|---|---|---|---|",
     ]
+    fused_avg_ns = None
     for (name, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         short = name.replace("(anonymous namespace)::", "").split("(")[0]
         short = short.replace("void ", "").replace("iofa::", "")
@@ -267,14 +277,28 @@ def summarise_trace(trace_dir, index, spec, bench_args):
         rate = ""
         if _is_fused({"Kernel_Name": name, "Grid_Size": grid}, spec):
             rate = f"{flops / (sum(ns) / len(ns) * 1e-9) / 1e12:.1f}"
+            fused_avg_ns = sum(ns) / len(ns)
         lines.append(f"| {short} | {grid} | {len(ns)} | {sum(ns) / len(ns):.0f} | {min(ns)} | "
                      f"{max(ns)} | {rate} |")
+    if bench_line is not None and fused_avg_ns is not None:
+        ev_ms = bench_line["fused_launch_ms"]
+        lines += [
+            "",
+            "The same run's bench line timed the fused launches with HIP events on the launch "
+            f"stream: mean {ev_ms:.5f} ms (median {bench_line['fused_launch_ms_median']:.5f}), "
+            f"roofline.achieved {bench_line['roofline']['achieved']} TFLOP/s; the kernel "
+            f"trace's average of all the fused dispatches above is {fused_avg_ns * 1e-6:.5f} ms "
+            f"(trace / events = {fused_avg_ns * 1e-6 / ev_ms:.3f}).",
+        ]
     lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
     path = os.path.join(ROOT, f"profiles/kernel_trace_{tag}.md")
     with open(path, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines))
     print(path)
 
+
+# file name of a profiled run's stdout kept beside its kernel trace
+BENCH_STDOUT = "bench_stdout.txt"
 
 # the traffic passes run the fused and the naive paths only, a few launches each
 TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-softmax --no-backward --no-fp8 "
