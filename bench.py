@@ -224,10 +224,13 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
     print(path)
 
 
-def summarise_trace(trace_dir, index, spec, bench_args):
+def summarise_trace(trace_dir, index, spec, bench_args, out_dir=None):
     """Per-kernel durations from rocprofv3's kernel_trace.csv, one row per
     kernel and launch grid, with the fused kernel's rate at the algorithmic
-    FLOP count for the workload's grid."""
+    FLOP count for the workload's grid.  When the profiled run's stdout was
+    kept beside the trace, its bench line's HIP-event launch average is quoted
+    next to the trace's average.  Writes profiles/kernel_trace_<tag>.md (or
+    into out_dir) and returns its path."""
     import csv
     import glob
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
@@ -291,10 +294,11 @@ def summarise_trace(trace_dir, index, spec, bench_args):
             f"(trace / events = {fused_avg_ns * 1e-6 / ev_ms:.3f}).",
         ]
     lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
-    path = os.path.join(ROOT, f"profiles/kernel_trace_{tag}.md")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernel_trace_{tag}.md")
     with open(path, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines))
     print(path)
+    return path
 
 
 # file name of a profiled run's stdout kept beside its kernel trace

@@ -68,3 +68,48 @@ def test_more_than_one_gpu_is_refused():
     assert proc.returncode == 2
     assert "one GPU" in proc.stderr
     assert proc.stdout == ""
+
+
+def _fake_trace(directory, fused_ns, other_ns):
+    # the columns of rocprofv3's kernel_trace.csv that the summary reads
+    spec = WORKLOADS[3]
+    grid = bench.fused_grid_items(spec)
+    rows = ["Kernel_Name,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp"]
+    t = 1000
+    for ns in fused_ns:
+        rows.append(f'"void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false>(...)",{grid},1,1,{t},{t + ns}')
+        t += ns + 10
+    for ns in other_ns:
+        rows.append(f'"void iofa::naive_pv_16<iofa::Bf16, 128>(...)",1024,1,1,{t},{t + ns}')
+        t += ns + 10
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "run_kernel_trace.csv"), "w") as fh:
+        fh.write("\n".join(rows) + "\n")
+
+
+def test_trace_summary_quotes_the_profiled_run(tmp_path):
+    # the fused rows' average (250 us here) is set against the bench line kept
+    # beside the trace (250 us from events), and the rate uses 4*B*H*N^2*d
+    trace = tmp_path / "kt"
+    _fake_trace(str(trace), [240_000, 260_000], [90_000])
+    line = {"fused_launch_ms": 0.25, "fused_launch_ms_median": 0.25,
+            "roofline": {"achieved": 1099.5}}
+    (trace / bench.BENCH_STDOUT).write_text("[bench] log line\n" + __import__("json").dumps(line) + "\n")
+    out = tmp_path / "out"
+    out.mkdir()
+    path = bench.summarise_trace(str(trace), 3, WORKLOADS[3], "--no-cpu-baseline", out_dir=str(out))
+    text = open(path).read()
+    assert path.startswith(str(out))
+    assert "| 2 | 250000 | 240000 | 260000 | 1099.5 |" in text
+    assert "trace / events = 1.000" in text
+    assert f"> {trace / bench.BENCH_STDOUT}" in text
+
+
+def test_trace_summary_without_the_profiled_run(tmp_path):
+    trace = tmp_path / "kt"
+    _fake_trace(str(trace), [250_000], [])
+    out = tmp_path / "out"
+    out.mkdir()
+    text = open(bench.summarise_trace(str(trace), 3, WORKLOADS[3], "", out_dir=str(out))).read()
+    assert "trace / events" not in text
+    assert bench.BENCH_STDOUT not in text
