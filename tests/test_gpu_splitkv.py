@@ -129,3 +129,36 @@ def test_merge_entry_point(out_dtype, d, dev):
         assert np.all(got[empty] == 0)
         fin = ~empty
         assert np.abs(got_lse[fin] - lse_ref[fin]).max() <= 1e-5 * (1 + np.abs(lse_ref[fin]).max())
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+def test_key_blocking_does_not_change_the_result(dtype, d, dev):
+    # Any division of the keys into blocks gives the same exact attention (the
+    # online recurrence adds blocks one at a time, [xinc] "7. Online Softmax",
+    # and [jiahao] "增量求解 softmax" merges any two).  The split-KV forward cuts
+    # the key tiles into G ranges and merges them, so every G is a different
+    # blocking and summation order: each meets the parity bar against the
+    # oracle and against the fused kernel's result; G = 1 runs the fused kernel.
+    N = 1000                                      # ragged: not a multiple of 32 or 64
+    q, k, v = make_qkv(1, 4, N, d, dtype, seed_base=4242 + d)
+    scale = default_scale(d)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o_f, lse_f = iofa.forward(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o_f.cpu(), lse_f.cpu(), o_ref, lse_ref, q.dtype, f"fused {dtype} d={d}")
+    tol = TOL[q.dtype]
+    for g in (1, 2, 3, 5, 8):
+        assert iofa.fa_splitkv_num_splits(1, 4, N, d, q.dtype, g) == g
+        _say(f"blocking {dtype} d={d} N={N} G={g}")
+        o, lse = iofa.forward_splitkv(qd, kd, vd, scale, g)
+        torch.cuda.synchronize()
+        if g == 1:
+            assert torch.equal(o, o_f) and torch.equal(lse, lse_f)
+            continue
+        assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"splitkv G={g}")
+        diff = (o.float() - o_f.float()).abs()
+        assert diff.max().item() <= tol["o_abs"], (g, diff.max().item())
+        rel = (torch.linalg.norm(o.float() - o_f.float()) / torch.linalg.norm(o_f.float())).item()
+        assert rel <= tol["o_relf"], (g, rel)
+        assert (lse - lse_f).abs().max().item() <= tol["lse_abs"], g
