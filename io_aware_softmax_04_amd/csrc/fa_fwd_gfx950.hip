@@ -23,7 +23,9 @@
 //     so rows past N arrive as zeros) into two stages each;
 //   * three-stage software pipeline: while the VALU computes the softmax of
 //     tile j, the MFMA unit runs P_{j-1} V_{j-1} and the scores of tile j+1,
-//     none of which depend on that softmax; one barrier per tile;
+//     none of which depend on that softmax; one barrier per tile; the score
+//     and P V products alternate, and the wave runs them at raised issue
+//     priority, dropped for the wait and barrier that close the tile;
 //   * the loop is unrolled by two so every LDS stage offset is a constant:
 //     each LDS read is a per-lane address computed once plus an immediate;
 //   * exponentials are exp2 with log2(e) folded into the fp32 scale; the row
