@@ -79,6 +79,13 @@ def test_backward_at_the_benchmark_head_shape(dev):
     check_backward(1, 2, 4096, 128, "bf16", seed=4096, dev=dev, label="bf16 H2 N4096")
 
 
+def test_backward_at_the_benchmark_workload(dev):
+    # the whole benchmarked workload (B = 2, H = 16, N = 4096, d = 128: the
+    # grid the bench times, 1024 workgroups per kernel), every gradient
+    # against the fp64 oracle (about 20 s of host time)
+    check_backward(2, 16, 4096, 128, "bf16", seed=3000, dev=dev, label="bf16 B2 H16 N4096")
+
+
 def test_softmax_longest_rows(dev):
     g = torch.Generator().manual_seed(5)
     x = (torch.randn((2, 1 << 27), generator=g) * 4).to(torch.bfloat16)
