@@ -108,3 +108,20 @@ def test_softmax_stress_spread(dev):
         y, lse = iofa.softmax(x.to(dev), want_lse=True)
         torch.cuda.synchronize()
         _check(x, y, lse, f"stress {dtype}")
+
+
+@pytest.mark.parametrize("rows,n,picked", [(32768, 8192, 48), (64, 1 << 22, 3)])
+def test_softmax_at_the_benchmarked_shapes(rows, n, picked, dev):
+    # the two shapes the bench times (rows of one chunk, and rows of 512
+    # chunks through the two-pass path), in the same launch configuration;
+    # rows are independent, so sampled rows (and the first and last) are held
+    # to the oracle's softmax of those rows
+    x = _inputs(rows, n, "bf16", seed=rows + 1, spread=4.0)
+    xd = x.to(dev)
+    y, lse = iofa.softmax(xd, want_lse=True)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(rows)
+    sel = np.unique(np.concatenate([[0, rows - 1], g.choice(rows, picked, replace=False)]))
+    print(f"softmax bf16 {rows}x{n}: checking {sel.size} rows", flush=True)
+    _check(x[sel], y.cpu()[sel], lse.cpu()[sel], f"bf16 {rows}x{n} sampled rows")
+    del xd, y
