@@ -19,6 +19,15 @@ namespace {
 constexpr int kQRows = 128;        // query rows per workgroup (4 waves x 32)
 constexpr int kKeysPerWg = 256;    // keys per workgroup in kernel 1
 constexpr int kMaxChunks = 16;     // 8-element chunks per thread in kernel 2 (N <= 32768)
+// S and P are written with streaming (non-temporal) stores when one of them is
+// larger than the 256 MB last-level cache (MALL): there the next kernel's
+// reads miss it anyway, and streaming stores took the path at B2 H16 N4096
+// d128 (1 GiB each) from 952 to 882 us, 6% at N = 8191.  Smaller ones keep
+// normal stores, which leave them in the MALL for the next kernel (streaming
+// stores made B4 H16 N1024 d64, 128 MiB each, 5% slower).
+constexpr uint64_t kStreamBytes = uint64_t(256) << 20;
+// cache-policy operand of a buffer store: non-temporal
+constexpr int kCpolNT = 2;
 
 // K tile of BC rows x D 16-bit elements into LDS rows of stride KS elements
 // (kernel 1).  256 threads; each owns KCH 16-byte chunks; consecutive threads
@@ -76,12 +85,13 @@ __device__ inline void load8_16(const uint16_t* p, float* v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = E::to_f32(half_of(w, e));
 }
-template <class E>
+template <class E, bool STREAM>
 __device__ inline void store8_16(uint16_t* p, const float* v) {
   u32x4 w;
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = pack2(E::from_f32(v[2 * e]), E::from_f32(v[2 * e + 1]));
-  *reinterpret_cast<u32x4*>(p) = w;
+  if constexpr (STREAM) __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = w;
 }
 
 __device__ inline float block_reduce(float x, bool is_max, float* red) {
@@ -102,7 +112,7 @@ __device__ inline float block_reduce(float x, bool is_max, float* red) {
 
 // ------------------------------------------------------- kernel 1 (16-bit)
 
-template <class T, int D>
+template <class T, int D, bool STREAM>
 __global__ __launch_bounds__(256, 4) void naive_scores_16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     uint16_t* __restrict__ S, int N, int ldS, int qtiles, int ktiles, int num_wg,
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(256, 4) void naive_scores_16(
                                ? (static_cast<uint32_t>(r) * ldS + key) * 2u : sbytes;
       __builtin_amdgcn_raw_buffer_store_b128(
           *reinterpret_cast<const u32x4*>(Ss + r * SS + 8 * (c % CPR)),
-          srsrc, static_cast<int>(off), 0, 0);
+          srsrc, static_cast<int>(off), 0, STREAM ? kCpolNT : 0);
     }
     __syncthreads();
   }
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(256, 4) void naive_scores_16(
 // MAXC: 8-element chunks per thread the row needs (a power of two, at most
 // kMaxChunks); instances for short rows hold fewer registers, so more rows
 // are in flight per CU.
-template <class E, int MAXC>
+template <class E, int MAXC, bool STREAM>
 __global__ __launch_bounds__(256) void naive_softmax_16(
     const uint16_t* __restrict__ S, uint16_t* __restrict__ P, float* __restrict__ LSE,
     int N, int ldS) {
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(256) void naive_softmax_16(
       float w[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = v[i][e] * inv;
-      store8_16<E>(p + c * 8, w);
+      store8_16<E, STREAM>(p + c * 8, w);
     }
   }
   if (LSE != nullptr && threadIdx.x == 0) LSE[row] = mx + logf(sum);
@@ -431,43 +441,51 @@ __global__ __launch_bounds__(256) void naive_pv_f32(
 
 // ---------------------------------------------------------------- launch
 
-template <class E, int MAXC>
+template <class E, int MAXC, bool STREAM>
 hipError_t launch_naive_softmax16_c(const NaiveArgs& a, int N, int ldS) {
-  hipLaunchKernelGGL((naive_softmax_16<E, MAXC>), dim3(static_cast<unsigned>(a.f.BH * N)),
+  hipLaunchKernelGGL((naive_softmax_16<E, MAXC, STREAM>), dim3(static_cast<unsigned>(a.f.BH * N)),
                      dim3(256), 0, a.f.stream, static_cast<const uint16_t*>(a.S),
                      static_cast<uint16_t*>(a.P), a.f.LSE, N, ldS);
   return hipGetLastError();
 }
 
-template <class E>
+template <class E, bool STREAM>
 hipError_t launch_naive_softmax16(const NaiveArgs& a, int N, int ldS) {
   const int per_thread = (ldS / 8 + 255) / 256;   // chunks per thread the row needs
-  if (per_thread <= 1) return launch_naive_softmax16_c<E, 1>(a, N, ldS);
-  if (per_thread <= 2) return launch_naive_softmax16_c<E, 2>(a, N, ldS);
-  if (per_thread <= 4) return launch_naive_softmax16_c<E, 4>(a, N, ldS);
-  if (per_thread <= 8) return launch_naive_softmax16_c<E, 8>(a, N, ldS);
-  return launch_naive_softmax16_c<E, kMaxChunks>(a, N, ldS);
+  if (per_thread <= 1) return launch_naive_softmax16_c<E, 1, STREAM>(a, N, ldS);
+  if (per_thread <= 2) return launch_naive_softmax16_c<E, 2, STREAM>(a, N, ldS);
+  if (per_thread <= 4) return launch_naive_softmax16_c<E, 4, STREAM>(a, N, ldS);
+  if (per_thread <= 8) return launch_naive_softmax16_c<E, 8, STREAM>(a, N, ldS);
+  return launch_naive_softmax16_c<E, kMaxChunks, STREAM>(a, N, ldS);
 }
 
-template <class T, class E, int D>
-hipError_t launch_naive16(const NaiveArgs& a) {
+template <class T, class E, int D, bool STREAM>
+hipError_t launch_naive16_s(const NaiveArgs& a) {
   const FwdArgs& f = a.f;
   const int N = static_cast<int>(f.N), ldS = static_cast<int>(a.ldS);
   const int qtiles = (N + kQRows - 1) / kQRows;
   const int ktiles = (N + kKeysPerWg - 1) / kKeysPerWg;
   const int wg1 = static_cast<int>(f.BH * qtiles * ktiles);
-  hipLaunchKernelGGL((naive_scores_16<T, D>), dim3(wg1), dim3(256), 0, f.stream,
+  hipLaunchKernelGGL((naive_scores_16<T, D, STREAM>), dim3(wg1), dim3(256), 0, f.stream,
                      static_cast<const uint16_t*>(f.Q), static_cast<const uint16_t*>(f.K),
                      static_cast<uint16_t*>(a.S), N, ldS, qtiles, ktiles, wg1, f.scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_naive_softmax16<E>(a, N, ldS);
+  e = launch_naive_softmax16<E, STREAM>(a, N, ldS);
   if (e != hipSuccess) return e;
   const int wg3 = static_cast<int>(f.BH * qtiles);
   hipLaunchKernelGGL((naive_pv_16<T, D>), dim3(wg3), dim3(256), 0, f.stream,
                      static_cast<const uint16_t*>(a.P), static_cast<const uint16_t*>(f.V),
                      static_cast<uint16_t*>(f.O), N, ldS, qtiles, wg3);
   return hipGetLastError();
+}
+
+template <class T, class E, int D>
+hipError_t launch_naive16(const NaiveArgs& a) {
+  const uint64_t s_bytes = static_cast<uint64_t>(a.f.BH) * static_cast<uint64_t>(a.f.N) *
+                           static_cast<uint64_t>(a.ldS) * 2u;
+  return s_bytes > kStreamBytes ? launch_naive16_s<T, E, D, true>(a)
+                                : launch_naive16_s<T, E, D, false>(a);
 }
 
 hipError_t launch_naive32(const NaiveArgs& a) {
