@@ -86,6 +86,14 @@ def test_backward_at_the_benchmark_workload(dev):
     check_backward(2, 16, 4096, 128, "bf16", seed=3000, dev=dev, label="bf16 B2 H16 N4096")
 
 
+def test_backward_at_the_numerics_stress_workload(dev):
+    # the numerics-stress workload at full size (B = 2, H = 8, N = 8191, not a
+    # tile multiple, fp16, scores spanning about +-60), every gradient against
+    # the fp64 oracle (about 30 s of host time)
+    check_backward(2, 8, 8191, 128, "fp16", seed=5000, dev=dev, dist="stress",
+                   label="stress fp16 B2 H8 N8191")
+
+
 def test_softmax_longest_rows(dev):
     g = torch.Generator().manual_seed(5)
     x = (torch.randn((2, 1 << 27), generator=g) * 4).to(torch.bfloat16)
