@@ -749,3 +749,78 @@ def test_planted_fp8_mistakes_fail_a_pin(kind, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"mutant {kind!r} passed every pin"
+
+
+# -------------------------------------------- FP8 inputs, selected query rows
+
+def _fp8_rows_brute(q8, k8, v8, scale, sq, sk, sv, rows):
+    """Plain loops over the selected rows of every head: values decoded by
+    torch's float8_e4m3fn conversion, scales rounded to fp32 (what the GPU
+    receives) and widened."""
+    dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).double().numpy()  # noqa: E731
+    f32 = lambda x: float(np.float32(x))  # noqa: E731
+    q, k, v = f32(sq) * dec(q8), f32(sk) * dec(k8), f32(sv) * dec(v8)
+    B, H, N, d = q.shape
+    o = np.empty((B, H, len(rows), v.shape[3]))
+    lse = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            for r, i in enumerate(rows):
+                s = [f32(scale) * sum(q[b, h, i, c] * k[b, h, j, c] for c in range(d))
+                     for j in range(N)]
+                m = max(s)
+                f = [math.exp(x - m) for x in s]
+                l_ = sum(f)
+                for c in range(v.shape[3]):
+                    o[b, h, r, c] = sum(f[j] * v[b, h, j, c] for j in range(N)) / l_
+                lse[b, h, r] = m + math.log(l_)
+    return o, lse
+
+
+def fp8_rows_pin_holds(rows_fn):
+    """The selected-rows form of the FP8 oracle against (1) plain loops on
+    those rows, with tensor and softmax scales that fp32 does not hold
+    exactly (so a scale used without its fp32 rounding moves the result by
+    ~1e-8 relative, far above the 1e-12 bar), and (2) the full form on the
+    same rows, for row lists that are unsorted, repeated and not a prefix."""
+    q8, k8, v8 = _fp8_tiny(11, B=2, H=2, N=13, d=6)
+    scale, sq, sk, sv = 0.1, 1.0 / 3.0, 0.7, 2.0 / 7.0
+    for rows in ([12, 0, 5], [3, 3, 9, 1], [7]):
+        rows = np.array(rows)
+        o, lse = rows_fn(q8, k8, v8, scale, sq, sk, sv, rows)
+        bo, bl = _fp8_rows_brute(q8, k8, v8, scale, sq, sk, sv, rows)
+        assert o.shape == bo.shape and lse.shape == bl.shape
+        assert np.abs(o - bo).max() <= 1e-12 * (1 + np.abs(bo).max())
+        assert np.abs(lse - bl).max() <= 1e-12 * (1 + np.abs(bl).max())
+        fo, fl = oracle.fp8_attention(q8, k8, v8, scale, sq, sk, sv)
+        assert np.abs(o - fo[:, :, rows]).max() <= 1e-13 * (1 + np.abs(fo).max())
+        assert np.abs(lse - fl[:, :, rows]).max() <= 1e-13 * (1 + np.abs(fl).max())
+    return True
+
+
+def test_fp8_attention_rows_pinned():
+    assert fp8_rows_pin_holds(oracle.fp8_attention_rows)
+
+
+@pytest.mark.parametrize("kind", ["rows_ignored", "scale_not_widened_from_fp32",
+                                  "tensor_scales_not_widened", "rows_of_first_head"])
+def test_planted_fp8_rows_mistakes_fail_the_pin(kind):
+    import oracle.fp8 as of
+
+    def mutant(q8, k8, v8, scale, q_scale, k_scale, v_scale, rows):
+        if kind == "tensor_scales_not_widened":
+            q, k, v = (q_scale * of.decode_e4m3(q8), k_scale * of.decode_e4m3(k8),
+                       v_scale * of.decode_e4m3(v8))
+        else:
+            q, k, v = of.fp8_values(q8, k8, v8, q_scale, k_scale, v_scale)
+        s = float(np.float32(scale)) if kind != "scale_not_widened_from_fp32" else scale
+        if kind == "rows_ignored":
+            rows = np.arange(len(rows))
+        o, lse = oracle.standard_attention_rows(q, k, v, s, rows)
+        if kind == "rows_of_first_head":
+            o, lse = o.copy(), lse.copy()
+            o[:, 1:], lse[:, 1:] = o[:, :1], lse[:, :1]
+        return o, lse
+
+    with pytest.raises(AssertionError):
+        fp8_rows_pin_holds(mutant)
