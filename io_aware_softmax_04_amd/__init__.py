@@ -316,6 +316,10 @@ def fa_naive_fwd(q, k, v, o, lse, s_ws, p_ws, scale, stream=None):
     fa_naive_workspace_bytes() bytes each; lse may be None."""
     lib = load_library()
     B, H, N, d = _shape(q, k, v, o)
+    # the softmax kernel writes B*H*N fp32 values through lse when it is given
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, H, N)):
+        raise ValueError("lse must be None or a contiguous fp32 (B, H, N) tensor")
     need = fa_naive_workspace_bytes(B, H, N, q.dtype)
     for name, ws in (("s_ws", s_ws), ("p_ws", p_ws)):
         if ws.numel() * ws.element_size() < need:

@@ -188,10 +188,11 @@ __device__ inline float2 chunk_stats(const float* v, float* red) {
   return make_float2(m, l);
 }
 
-// Rows of at most one chunk: read once, write once.
+// Rows of at most one chunk: read once, write once.  X and Y may be the same
+// buffer (an in-place call), so neither is declared __restrict__: each thread
+// reads its elements before it writes them, and no other thread touches them.
 template <int KIND, bool VECTOR>
-__global__ __launch_bounds__(kThreads) void softmax_short_kernel(const void* __restrict__ X,
-                                                                 void* __restrict__ Y,
+__global__ __launch_bounds__(kThreads) void softmax_short_kernel(const void* X, void* Y,
                                                                  float* __restrict__ LSE,
                                                                  int64_t n) {
   using E = Elem<KIND>;
@@ -224,10 +225,11 @@ __global__ __launch_bounds__(kThreads) void softmax_stats_kernel(const void* __r
   if (threadIdx.x == 0) stats[r * chunks + c] = ml;
 }
 
-// Long rows, pass 2: merge row r's chunk pairs, write its chunk c.
+// Long rows, pass 2: merge row r's chunk pairs, write its chunk c.  X and Y
+// may be the same buffer (in place), as in softmax_short_kernel.
 template <int KIND, bool VECTOR>
 __global__ __launch_bounds__(kThreads) void softmax_normalize_kernel(
-    const void* __restrict__ X, void* __restrict__ Y, float* __restrict__ LSE,
+    const void* X, void* Y, float* __restrict__ LSE,
     const float2* __restrict__ stats, int64_t n, int chunks) {
   using E = Elem<KIND>;
   __shared__ float2 red2[4];

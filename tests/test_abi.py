@@ -327,3 +327,26 @@ def test_binding_refuses_host_tensors():
         iofa.fa_fwd(q, q, q, torch.empty_like(q), torch.empty(1, 1, 8), 0.125)
     with pytest.raises(ValueError):
         iofa.softmax(torch.zeros(2, 10))
+
+
+@pytest.mark.parametrize("bad", ["fp16", "short", "strided"])
+def test_naive_binding_checks_lse_before_the_library(bad, monkeypatch):
+    # a wrong lse would take B*H*N fp32 writes past its end: the binding
+    # refuses it before any call into the library
+    import torch
+    lib = iofa.load_library()
+
+    class Refuse:
+        def __getattr__(self, name):
+            if name == "fa_naive_workspace_bytes":
+                return lib.fa_naive_workspace_bytes
+            raise AssertionError(f"library reached: {name}")
+
+    monkeypatch.setattr(iofa, "_lib", Refuse())
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = {"fp16": torch.empty(1, 2, 8, dtype=torch.float16),
+           "short": torch.empty(1, 2, 7),
+           "strided": torch.empty(1, 2, 16)[..., ::2]}[bad]
+    ws = torch.empty(1 << 12, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="lse"):
+        iofa.fa_naive_fwd(q, q, q, torch.empty_like(q), lse, ws, ws, 0.125)
