@@ -175,7 +175,7 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream);
 
 /* The G that fa_fwd_splitkv uses for `requested` (see above); 0 for invalid
- * sizes or dtype. */
+ * sizes (including sizes beyond the limits above) or dtype. */
 int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested);
 
 /* Workspace bytes fa_fwd_splitkv needs: G * B*H*N * (d + 1) * 4 for the G it
@@ -231,7 +231,8 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes fa_softmax_rows needs: rows * chunks * 8 for rows longer
- * than one chunk, else 0 (also for invalid arguments). */
+ * than one chunk, else 0 (also for invalid arguments and sizes that do not
+ * fit size_t). */
 size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype);
 
 /*
@@ -262,12 +263,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            const float* LSE, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream);
 
-/* Workspace bytes of fa_bwd: B * H * N * 8 (0 for negative sizes). */
+/* Workspace bytes of fa_bwd: B * H * N * 8 (0 for negative sizes or a
+ * size that does not fit size_t). */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /* Bytes of ONE naive workspace (S or P): B * H * N * ldS * sizeof(dtype),
- * ldS = N rounded up to a multiple of 8.  Returns 0 for an invalid dtype
- * or negative sizes. */
+ * ldS = N rounded up to a multiple of 8.  Returns 0 for an invalid dtype,
+ * negative sizes, N above the naive path's limit (32768) or a size that does
+ * not fit size_t. */
 size_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype);
 
 /* Static English text for an fa_status value ("unknown status" otherwise). */

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "fa_launch.h"
@@ -36,7 +37,29 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Only for 0 <= n <= kNaiveMaxN (callers check the bound first).
 int64_t round_up8(int64_t n) { return (n + 7) / 8 * 8; }
+
+// Ceiling of n / m for n >= 0, m > 0, without overflow for any int64 n.
+int64_t ceil_div(int64_t n, int64_t m) { return n / m + (n % m != 0); }
+
+// The product of the factors in size_t, or 0 when it does not fit.
+size_t product_or_zero(std::initializer_list<size_t> factors) {
+  size_t r = 1;
+  for (size_t f : factors)
+    if (__builtin_mul_overflow(r, f, &r)) return 0;
+  return r;
+}
+
+// Sizes within the library's limits -- B * H < 2^31, N * d < 2^31 and
+// B * H * N < 2^31 -- evaluated without signed overflow for any int64
+// input.  B, H, N >= 1 and d > 0 are the caller's to check first.
+bool within_limits(int64_t B, int64_t H, int64_t N, int64_t d) {
+  constexpr int64_t kLim = (int64_t(1) << 31) - 1;
+  if (B > kLim || H > kLim || B * H > kLim) return false;   // B, H < 2^31: no overflow
+  if (N > kLim / d) return false;                            // N * d < 2^31
+  return B * H * N <= kLim;                                  // < 2^31 * 2^31: no overflow
+}
 
 // Split-KV policy: at most this many key ranges, and enough of them that the
 // partial pass has about this many workgroups (two per CU on 256 CUs), but,
@@ -72,10 +95,10 @@ int check_common(const void* Q, const void* K, const void* V, const void* O, con
     *empty = true;
     return FA_OK;
   }
-  if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX)
-    return fail(FA_ERR_SHAPE, "B * H must be < 2^31");
-  if (N * d >= (int64_t(1) << 31)) return fail(FA_ERR_SHAPE, "N * d must be < 2^31");
-  if (B * H * N >= (int64_t(1) << 31)) return fail(FA_ERR_SHAPE, "B * H * N must be < 2^31");
+  if (!within_limits(B, H, N, d))
+    return fail(FA_ERR_SHAPE, "B * H, N * d and B * H * N must each be < 2^31 (got B=" +
+                                  std::to_string(B) + " H=" + std::to_string(H) +
+                                  " N=" + std::to_string(N) + ")");
   if (!Q || !K || !V || !O) return fail(FA_ERR_NULL, "Q, K, V and O must not be NULL");
   if (lse_required && !LSE) return fail(FA_ERR_NULL, "LSE must not be NULL");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
@@ -154,7 +177,8 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
 
 int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested) {
   if (elem_bytes(dtype) == 0 || B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const int64_t tiles = (N + iofa::fused_key_tile(dtype, d) - 1) / iofa::fused_key_tile(dtype, d);
+  if (!within_limits(B, H, N, d)) return 0;
+  const int64_t tiles = ceil_div(N, iofa::fused_key_tile(dtype, d));
   const int64_t cap = tiles < kMaxSplits ? tiles : kMaxSplits;
   int64_t g = requested;
   if (g <= 0) {
@@ -173,6 +197,7 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, in
                                   int num_splits) {
   const int g = fa_splitkv_num_splits(B, H, N, d, dtype, num_splits);
   if (g <= 1) return 0;
+  // g > 1 only for sizes within the limits, so the product fits
   const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N);
   return static_cast<size_t>(g) * rows * (static_cast<size_t>(d) + 1) * sizeof(float);
 }
@@ -225,7 +250,8 @@ int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts,
   if (d != 64 && d != 128)
     return fail(FA_ERR_HEAD_DIM, "head dimension d must be 64 or 128 (got " + std::to_string(d) + ")");
   if (rows == 0) return FA_OK;
-  if (rows * num_parts * (d + 1) >= (int64_t(1) << 40)) return fail(FA_ERR_SHAPE, "too many rows");
+  if (rows > ((int64_t(1) << 40) - 1) / (num_parts * (d + 1)))
+    return fail(FA_ERR_SHAPE, "too many rows");
   if (!O_part || !LSE_part || !O || !LSE) return fail(FA_ERR_NULL, "pointers must not be NULL");
   if (!aligned(O_part, 16) || !aligned(O, 16)) return fail(FA_ERR_ALIGN, "O_part and O must be 16-byte aligned");
   if (!aligned(LSE_part, 4) || !aligned(LSE, 4)) return fail(FA_ERR_ALIGN, "LSE_part and LSE must be 4-byte aligned");
@@ -272,7 +298,8 @@ size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype) {
   if (elem_bytes(dtype) == 0 || rows < 0 || n < 0) return 0;
   const int64_t chunk = iofa::softmax_chunk(dtype);
   if (n <= chunk) return 0;
-  return static_cast<size_t>(rows) * static_cast<size_t>((n + chunk - 1) / chunk) * 2 * sizeof(float);
+  return product_or_zero({static_cast<size_t>(rows), static_cast<size_t>(ceil_div(n, chunk)),
+                          2 * sizeof(float)});
 }
 
 int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n, int dtype,
@@ -284,8 +311,8 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
   if (rows < 0 || n < 0) return fail(FA_ERR_SHAPE, "rows and n must be >= 0");
   if (rows == 0 || n == 0) return FA_OK;
   const int64_t chunk = iofa::softmax_chunk(dtype);
-  const int64_t chunks = (n + chunk - 1) / chunk;
-  if (rows * chunks >= (int64_t(1) << 31) || chunks >= (int64_t(1) << 31))
+  const int64_t chunks = ceil_div(n, chunk);
+  if (chunks > INT32_MAX || rows > INT32_MAX / chunks)   // rows * chunks < 2^31
     return fail(FA_ERR_SHAPE, "too many workgroups");
   if (!X || !Y) return fail(FA_ERR_NULL, "X and Y must not be NULL");
   if (!aligned(X, e) || !aligned(Y, e)) return fail(FA_ERR_ALIGN, "X and Y must be element-aligned");
@@ -317,7 +344,8 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B < 0 || H < 0 || N < 0) return 0;
-  return static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N) * 2 * sizeof(float);
+  return product_or_zero({static_cast<size_t>(B), static_cast<size_t>(H), static_cast<size_t>(N),
+                          2 * sizeof(float)});
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -354,9 +382,9 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 
 size_t fa_naive_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
   const int e = elem_bytes(dtype);
-  if (e == 0 || B < 0 || H < 0 || N < 0) return 0;
-  return static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N) *
-         static_cast<size_t>(round_up8(N)) * static_cast<size_t>(e);
+  if (e == 0 || B < 0 || H < 0 || N < 0 || N > iofa::kNaiveMaxN) return 0;
+  return product_or_zero({static_cast<size_t>(B), static_cast<size_t>(H), static_cast<size_t>(N),
+                          static_cast<size_t>(round_up8(N)), static_cast<size_t>(e)});
 }
 
 const char* fa_status_string(int status) {
