@@ -53,10 +53,9 @@ def test_splitkv_one_gpu_share_of_the_headline_workload(dev):
     assert iofa.fa_splitkv_num_splits(2, 2, 4096, 128, q.dtype, 0) == 4
     o, lse = iofa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), scale)
     torch.cuda.synchronize()
-    rows = sample_rows(4096, seed=3)
-    o_ref, lse_ref = oracle_rows(q, k, v, scale, rows)
-    res = assert_parity(o.cpu()[:, :, rows], lse.cpu()[:, :, rows], o_ref, lse_ref, q.dtype,
-                        "splitkv B2 H2 N4096")
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    res = assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype,
+                        "splitkv B2 H2 N4096 (every element)")
     _say(f"  max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
 
 
