@@ -470,6 +470,54 @@ def time_graph(fn, torch, reps=20, replays=10, warm_seconds=0.3):
     return e0.elapsed_time(e1) / (reps * replays)
 
 
+HEADLINE_WARM_S = 0.6
+CLOCK_WINDOW_TICKS = 2_500_000       # 25 ms of the 100 MHz real-time counter
+
+
+def shader_clock_under(fn, torch, iofa, dev, launches=200):
+    """The shader clock while ``fn``'s kernels run back to back: ``launches``
+    calls (about 50 ms at the headline workload) are queued on the current
+    stream, then the clock probe (one sleeping wave, built as
+    _lib/libiofa_clock.so) is started on a side stream for a 25 ms window
+    that those calls cover.  Runs after the headline timing, so it does not
+    share the GPU with the timed steps.  Returns None when the probe library
+    is missing."""
+    import ctypes
+    path = os.path.join(os.path.dirname(iofa.library_path()), "libiofa_clock.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.iofa_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    lib.iofa_clock_probe.restype = ctypes.c_int
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        fn()
+    # the side stream does not wait for those calls: the probe runs beside them
+    st = lib.iofa_clock_probe(ctypes.c_void_p(out.data_ptr()), CLOCK_WINDOW_TICKS,
+                              ctypes.c_void_p(side.cuda_stream))
+    torch.cuda.synchronize()
+    if st != 0:
+        raise RuntimeError(f"clock probe failed with status {st}")
+    cyc, ticks = (int(x) for x in out.cpu())
+    return {"shader_clock_mhz": round(100.0 * cyc / ticks, 1) if ticks else None,
+            "window_ms": round(ticks / 1e5, 2),
+            "how": f"s_memtime / s_memrealtime of one sleeping wave on a side stream while "
+                   f"{launches} fused launches run"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
     """Time the fp64 oracle on a bounded sample (all heads, a prefix of query
     rows sized for about ``target_s`` seconds) and check the GPU output on
@@ -507,6 +555,9 @@ def cpu_baseline(q, k, v, scale, spec, o_gpu, lse_gpu, target_s):
         "sample": f"all {B * H} heads, query rows 0..{rows_n - 1} of {N} "
                   f"({rows_n / N:.1%} of the workload's FLOPs), fp64 numpy/OpenBLAS",
         "seconds": round(t, 3),
+        "cpu_model": cpu_model(),
+        "cores_note": "BLAS threads of the fp64 products; the oracle's elementwise steps "
+                      "run on one thread",
         "host_cores_visible": len(os.sched_getaffinity(0)),
         "sample_parity": {
             "max_abs": float(np.abs(diff).max()),
@@ -719,7 +770,10 @@ def main():
         iofa.fa_fwd(qd, kd, vd, o, lse, scale)
 
     print(f"[bench] workload {args.workload}: {spec['name']}", file=sys.stderr, flush=True)
-    wall_ms, ev_ms, ev_med, ev_min = time_launches(fused, args.steps, args.warmup, torch)
+    # the timed steps start only after at least HEADLINE_WARM_S of sustained
+    # launches, whatever --warmup asks for, so they see the settled clock
+    wall_ms, ev_ms, ev_med, ev_min = time_launches(fused, args.steps, args.warmup, torch,
+                                                   warm_seconds=HEADLINE_WARM_S)
     print(f"[bench] fused: {wall_ms:.4f} ms/step wall, {ev_ms:.4f} ms/launch (events; "
           f"median {ev_med:.4f}, min {ev_min:.4f})", file=sys.stderr, flush=True)
     achieved = flops / (ev_ms * 1e-3) / 1e12
@@ -727,6 +781,11 @@ def main():
     peak = PEAK_BF16_TFLOPS if spec["dtype"] in ("bf16", "fp16") else 157.3
 
     traffic = read_traffic(spec)
+    clock = shader_clock_under(fused, torch, iofa, dev)
+    if clock is not None:
+        clock["achieved_over_peak_at_that_clock"] = round(
+            flops / (ev_ms * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS * clock["shader_clock_mhz"] / 2400.0),
+            4) if spec["dtype"] != "fp32" else None
 
     models = bytes_models(spec)
     line = {
@@ -750,6 +809,7 @@ def main():
         "fused_launch_ms_median": round(ev_med, 5),
         "fused_launch_ms_min": round(ev_min, 5),
         "fused_tflops_at_median": round(flops / (ev_med * 1e-3) / 1e12, 2),
+        "shader_clock": clock,
         "device": device_info(torch, dev),
         "bytes_models": models,
     }

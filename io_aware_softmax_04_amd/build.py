@@ -3,8 +3,9 @@
     python -m io_aware_softmax_04_amd.build
 
 Compiles every HIP source for gfx950 with hipcc and links one shared
-library at io_aware_softmax_04_amd/_lib/libiofa.so, plus the standalone
-MFMA-ceiling measurement program _lib/mfma_ceiling.  Packed fp32 vector
+library at io_aware_softmax_04_amd/_lib/libiofa.so, plus two measurement
+helpers that are not part of it: the standalone MFMA-ceiling program
+_lib/mfma_ceiling and the shader-clock probe _lib/libiofa_clock.so.  Packed fp32 vector
 instructions are disabled for all device code.
 """
 
@@ -22,6 +23,8 @@ OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libiofa.so")
 CEILING = os.path.join(OUT_DIR, "mfma_ceiling")
 CEILING_SOURCE = "mfma_ceiling.hip"
+CLOCK = os.path.join(OUT_DIR, "libiofa_clock.so")
+CLOCK_SOURCE = "clock_probe.hip"
 
 SOURCES = ["fa_api.cpp", "fa_fwd_gfx950.hip", "fa_naive_gfx950.hip", "fa_merge_gfx950.hip",
            "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip", "fa_fwd_fp8_gfx950.hip"]
@@ -84,6 +87,13 @@ def build(verbose=False, extra_flags=()):
     if rc != 0:
         raise RuntimeError(f"building mfma_ceiling failed:\n{out}")
     os.replace(tmp, CEILING)
+    tmp = CLOCK + ".tmp"
+    cmd = [cc, *COMMON, *extra_flags, "-shared", "-x", "hip", os.path.join(CSRC, CLOCK_SOURCE),
+           "-o", tmp]
+    rc, out = _run(cmd)
+    if rc != 0:
+        raise RuntimeError(f"building libiofa_clock.so failed:\n{out}")
+    os.replace(tmp, CLOCK)
     return LIB
 
 
