@@ -174,6 +174,30 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                    void* workspace, size_t workspace_bytes, int num_splits, int64_t B,
                    int64_t H, int64_t N, int64_t d, float scale, int dtype, void* stream);
 
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid the allocator.  The partials go to a scratch
+ * array the library itself holds, FA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU
+ * it runs on, in place from that device's first such call until the
+ * process ends.  The call allocates nothing and frees nothing.
+ *   num_splits  as fa_fwd_splitkv.  If the resolved G needs more than
+ *               FA_NOALLOC_SCRATCH_BYTES (fa_splitkv_workspace_bytes() tells
+ *               how much), the call returns FA_ERR_SHAPE and enqueues
+ *               nothing; num_splits = 1 needs no scratch at all.
+ * The scratch used is that of the calling thread's current device, and
+ * `stream` must belong to that device.  Every call on one GPU shares that
+ * GPU's array and leaves its partials there; nothing in it needs to start
+ * at zero.  Calls that overlap on one GPU (concurrent streams, or threads
+ * without ordering between their streams) race on the array and may return
+ * wrong results: order them.  Other arguments, results and errors as
+ * fa_fwd_splitkv; FA_ERR_HIP if the array's address cannot be obtained.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int num_splits, int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, int dtype, void* stream);
+
 /* The G that fa_fwd_splitkv uses for `requested` (see above); 0 for invalid
  * sizes (including sizes beyond the limits above) or dtype. */
 int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested);

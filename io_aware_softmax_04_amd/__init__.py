@@ -1,6 +1,7 @@
 """Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
 
-The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_splitkv_num_splits``,
+The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_fwd_splitkv_noalloc``,
+``fa_splitkv_num_splits``,
 ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
 ``fa_softmax_workspace_bytes``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_fp8``,
 ``fa_naive_fwd``,
@@ -25,7 +26,8 @@ import torch
 
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
-    "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
+    "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
+    "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
     "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "softmax",
     "fa_bwd", "fa_bwd_workspace_bytes", "backward", "fa_fwd_fp8", "forward_fp8",
     "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
@@ -73,6 +75,9 @@ def load_library():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                    i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, fp, ctypes.c_int, i64, i64, i64, i64,
+                                           ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.fa_splitkv_num_splits.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
@@ -208,6 +213,25 @@ def fa_fwd_splitkv(q, k, v, o, lse, workspace, scale, num_splits=0, stream=None)
                                 ws_bytes, int(num_splits), B, H, N, d, float(scale),
                                 _DTYPE_CODE[q.dtype], _stream(stream, q.device))
     _check(st)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, scale, num_splits=0, stream=None):
+    """Split-KV forward with its partials in the library's own scratch array
+    (FA_NOALLOC_SCRATCH_BYTES per GPU): no workspace argument, nothing
+    allocated.  Calls that overlap on one GPU race on that array."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o)
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous fp32 (B, H, N) tensor")
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse),
+                                        int(num_splits), B, H, N, d, float(scale),
+                                        _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def fa_splitkv_num_splits(B, H, N, d, dtype, requested=0):

@@ -27,7 +27,8 @@ CLOCK = os.path.join(OUT_DIR, "libiofa_clock.so")
 CLOCK_SOURCE = "clock_probe.hip"
 
 SOURCES = ["fa_api.cpp", "fa_fwd_gfx950.hip", "fa_naive_gfx950.hip", "fa_merge_gfx950.hip",
-           "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip", "fa_fwd_fp8_gfx950.hip"]
+           "fa_softmax_gfx950.hip", "fa_bwd_gfx950.hip", "fa_fwd_fp8_gfx950.hip",
+           "fa_scratch_gfx950.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -239,6 +239,34 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
   return hip_status(iofa::launch_merge(m), "split-KV merge launch");
 }
 
+static_assert(FA_NOALLOC_SCRATCH_BYTES == iofa::kScratchBytes,
+              "the header and the library state one scratch size");
+
+int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           int num_splits, int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  bool empty = false;
+  int st = check_common(Q, K, V, O, LSE, true, B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK || empty) return st;
+  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits);
+  if (need > FA_NOALLOC_SCRATCH_BYTES)
+    return fail(FA_ERR_SHAPE, "the " + std::to_string(fa_splitkv_num_splits(B, H, N, d, dtype,
+                                                                            num_splits)) +
+                                  "-way split needs " + std::to_string(need) +
+                                  " bytes of partials, more than the " +
+                                  std::to_string(FA_NOALLOC_SCRATCH_BYTES) +
+                                  "-byte scratch array: request fewer splits (1 needs none) "
+                                  "or call fa_fwd_splitkv with a workspace");
+  void* scratch = nullptr;
+  if (need > 0) {
+    st = hip_status(iofa::scratch_address(&scratch), "scratch array address");
+    if (st != FA_OK) return st;
+  }
+  return fa_fwd_splitkv(Q, K, V, O, LSE, scratch, need, num_splits, B, H, N, d, scale, dtype,
+                        stream);
+}
+
 int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts, int64_t rows,
                       int64_t d, void* O, float* LSE, int dtype, void* stream) {
   g_last_error.clear();

@@ -123,4 +123,12 @@ hipError_t launch_naive(const NaiveArgs& a);
 
 constexpr int64_t kNaiveMaxN = 32768;
 
+// Bytes of the library's own scratch array (fa_scratch_gfx950.hip), used by
+// the entry point that allocates nothing; FA_NOALLOC_SCRATCH_BYTES in
+// fa_api.h states the same size.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+// Device address of the current device's copy of that array (looked up once
+// per device, then cached).
+hipError_t scratch_address(void** ptr);
+
 }  // namespace iofa

@@ -7,7 +7,8 @@
 // pointers are fake device addresses that nothing dereferences: the kernel
 // launchers are replaced at link time (ld --wrap) by stand-ins that record
 // the call, check the arguments validation let through, and report a launch
-// error, so no call reaches a GPU.  The driver fails (exit 1) when a call
+// error, and the scratch array's address lookup returns a fake address, so
+// no call reaches a GPU.  The driver fails (exit 1) when a call
 // returns a status outside the enum, returns FA_OK for a non-empty problem
 // (the launch would have been reached), leaves no message for a failure, or
 // lets through arguments the launchers cannot take; the sanitizers abort on
@@ -80,6 +81,10 @@ hipError_t __wrap__ZN4iofa10launch_bwdERKNS_7BwdArgsE(const iofa::BwdArgs& a) {
                    (a.dtype == 1 || a.dtype == 2),
                "launch_bwd");
   return hipErrorInvalidValue;
+}
+hipError_t __wrap__ZN4iofa15scratch_addressEPPv(void** ptr) {
+  *ptr = reinterpret_cast<void*>(uintptr_t(1) << 50);   // a fake device address
+  return hipSuccess;
 }
 hipError_t __wrap__ZN4iofa10launch_fp8ERKNS_7Fp8ArgsE(const iofa::Fp8Args& a) {
   check_launch(a.Q && a.K && a.V && a.O && a.LSE && a.BH >= 1 && a.N >= 1 &&
@@ -167,6 +172,10 @@ int main() {
                                        dt, nullptr),
                         empty, "fa_fwd_splitkv");
                 }
+                for (int g : {0, 1, 4, 64})
+                  after(fa_fwd_splitkv_noalloc(p.q, p.k, p.v, p.o, p.lse, g, B, H, N, d, sc, dt,
+                                               nullptr),
+                        empty, "fa_fwd_splitkv_noalloc");
                 const size_t bw = fa_bwd_workspace_bytes(B, H, N);
                 after(fa_bwd(p.q, p.k, p.v, p.x1, p.x2, p.lse, p.o, p.x3, p.x4, p.ws, bw, B, H, N,
                              d, sc, dt, nullptr),

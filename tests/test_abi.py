@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fa_fwd", "fa_fwd_splitkv", "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
+        "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_splitkv_num_splits",
+        "fa_splitkv_workspace_bytes",
         "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_bwd",
         "fa_bwd_workspace_bytes", "fa_fwd_fp8", "fa_naive_fwd",
         "fa_naive_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version"])
@@ -350,3 +351,26 @@ def test_naive_binding_checks_lse_before_the_library(bad, monkeypatch):
     ws = torch.empty(1 << 12, dtype=torch.uint8)
     with pytest.raises(ValueError, match="lse"):
         iofa.fa_naive_fwd(q, q, q, torch.empty_like(q), lse, ws, ws, 0.125)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER, encoding="utf-8").read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert iofa.FA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    # bad arguments return before the scratch array's address is looked up
+    i64 = ctypes.c_int64
+    args = [A, A * 2, A * 3, A * 4, ctypes.cast(A * 5, ctypes.POINTER(ctypes.c_float))]
+    f = lib.fa_fwd_splitkv_noalloc
+    assert f(*args, 0, i64(1), i64(2), i64(100), i64(96), ctypes.c_float(0.1), 2, None) == 3
+    assert f(*args, 0, i64(1), i64(2), i64(100), i64(128), ctypes.c_float(0.1), 7, None) == 4
+    assert f(*args, 0, i64(-1), i64(2), i64(100), i64(128), ctypes.c_float(0.1), 2, None) == 2
+    assert f(None, *args[1:], 0, i64(1), i64(2), i64(100), i64(128), ctypes.c_float(0.1), 2,
+             None) == 1
+    # a split whose partials exceed the 64 MiB array is refused with a message
+    assert f(*args, 8, i64(8), i64(16), i64(4096), i64(128), ctypes.c_float(0.1), 2, None) == 2
+    assert "scratch" in iofa.fa_last_error()
+    # the empty problem is a no-op
+    assert f(*args, 0, i64(0), i64(2), i64(100), i64(128), ctypes.c_float(0.1), 2, None) == 0

@@ -16,14 +16,16 @@ PKG = os.path.join(ROOT, "io_aware_softmax_04_amd")
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 KERNEL_OBJECTS = ["fa_fwd_gfx950.o", "fa_naive_gfx950.o", "fa_merge_gfx950.o",
-                  "fa_softmax_gfx950.o", "fa_bwd_gfx950.o", "fa_fwd_fp8_gfx950.o"]
+                  "fa_softmax_gfx950.o", "fa_bwd_gfx950.o", "fa_fwd_fp8_gfx950.o",
+                  "fa_scratch_gfx950.o"]
 LAUNCHERS = ["_ZN4iofa12launch_fusedERKNS_7FwdArgsE",
              "_ZN4iofa20launch_fused_partialERKNS_7FwdArgsEiPfS3_",
              "_ZN4iofa12launch_mergeERKNS_9MergeArgsE",
              "_ZN4iofa12launch_naiveERKNS_9NaiveArgsE",
              "_ZN4iofa14launch_softmaxERKNS_11SoftmaxArgsE",
              "_ZN4iofa10launch_bwdERKNS_7BwdArgsE",
-             "_ZN4iofa10launch_fp8ERKNS_7Fp8ArgsE"]
+             "_ZN4iofa10launch_fp8ERKNS_7Fp8ArgsE",
+             "_ZN4iofa15scratch_addressEPPv"]
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
 
 
