@@ -66,11 +66,12 @@ def parse():
                         "into the kernel-trace summary under profiles/ and exit")
     p.add_argument("--trace-cmd", default="",
                    help="the bench.py arguments of that run (recorded in the summary)")
-    p.add_argument("--sq-from", metavar="PMC_DIR",
-                   help="summarise a `rocprofv3 --pmc` run of bench.py with SQ_BUSY_CYCLES, "
-                        "SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_INSTS_LDS, "
-                        "SQ_INSTS_VALU_TRANS_F32 and SQ_WAVES into the shader-counter summary "
-                        "under profiles/ (effective clock, MFMA busy fraction) and exit")
+    p.add_argument("--sq-from", nargs="+", metavar="PMC_DIR",
+                   help="summarise one or two `rocprofv3 --pmc` passes of bench.py (the "
+                        "counter sets SQ_PASSES a and b) into the shader-counter summary of "
+                        "--sq-kernel under profiles/ (effective clock, MFMA busy, waits) and exit")
+    p.add_argument("--sq-kernel", default="fused", choices=sorted(SQ_KERNELS),
+                   help="kernel the counter summary covers")
     p.add_argument("--copy-mib", type=int, default=1024,
                    help="size of the calibration copy in those runs")
     return p.parse_args()
@@ -307,85 +308,132 @@ BENCH_STDOUT = "bench_stdout.txt"
 # the traffic passes run the fused and the naive paths only, a few launches each
 TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-softmax --no-backward --no-fp8 "
                       "--no-ceiling --no-cpu-baseline")
-SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
-               "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES"]
+# Shader counters, in two rocprofv3 --pmc passes of at most 8 SQ counters each
+SQ_PASSES = {
+    "a": ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+          "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES", "SQ_WAVE_CYCLES"],
+    "b": ["SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS",
+          "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+          "SQ_INSTS_SALU"],
+}
 SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
-# the counter pass times the fused kernel only, after the default warm-up
-SQ_BENCH_ARGS = ("--steps 20 --no-naive --no-splitkv --no-softmax --no-backward --no-fp8 "
-                 "--no-ceiling --no-cpu-baseline")
 SIMDS = 1024                 # 256 CUs x 4
+# Kernels the counter summary covers: (name filter, FLOPs per MFMA instruction,
+# bench.py arguments of the counter passes, file tag)
+SQ_KERNELS = {
+    "fused": ("fused", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax --no-backward "
+              "--no-fp8 --no-ceiling --no-cpu-baseline", "fused_fwd"),
+    "bwd_dq": ("bwd_dq_kernel", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
+               "--no-fp8 --no-ceiling --no-cpu-baseline", "bwd_dq"),
+    "bwd_dkdv": ("bwd_dkdv_kernel", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
+                 "--no-fp8 --no-ceiling --no-cpu-baseline", "bwd_dkdv"),
+    "fp8": ("fa_fwd_fp8_kernel", 131072.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
+            "--no-backward --no-ceiling --no-cpu-baseline", "fp8_fwd"),
+}
 
 
-def summarise_sq(pmc_dir, index, spec):
-    """Effective shader clock and MFMA busy fraction of the fused kernel.
+def _sq_match(row, spec, which):
+    name = SQ_KERNELS[which][0]
+    if name == "fused":
+        return _is_fused(row, spec)
+    return name in row["Kernel_Name"]
+
+
+def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
+    """Shader counters of one kernel from one or more rocprofv3 --pmc passes.
 
     SQ_BUSY_CYCLES counts, per shader engine, the cycles any wave is
     resident; summed over the 32 engines and divided by 32 it is the
     kernel's length in shader cycles, so dividing by the dispatch's duration
     gives the clock it ran at.  SQ_VALU_MFMA_BUSY_CYCLES summed over the
     SIMDs, over SIMDs x kernel cycles, is the fraction of time the matrix
-    cores were busy."""
+    cores were busy; SQ_VALU_MFMA_COEXEC_CYCLES likewise the fraction in
+    which a vector instruction issued while they were busy.  SQ_WAVE_CYCLES,
+    SQ_WAIT_ANY and SQ_WAIT_INST_LDS are wave-cycles in units of 4 cycles:
+    their ratios are the fraction of a wave's lifetime spent waiting, and
+    waiting to issue an LDS instruction."""
     import csv
     import glob
-    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
     per = {}
-    for f in files:
-        with open(f, encoding="utf-8") as fh:
-            for r in csv.DictReader(fh):
-                if not _is_fused(r, spec):
-                    continue
-                d = per.setdefault(int(r["Dispatch_Id"]), {})
-                d[r["Counter_Name"]] = float(r["Counter_Value"])
-                d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    for d in pmc_dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            with open(f, encoding="utf-8") as fh:
+                rows = [r for r in csv.DictReader(fh) if _sq_match(r, spec, which)]
+            # dispatches of one pass, in order; passes are matched by position
+            ids = sorted({int(r["Dispatch_Id"]) for r in rows})
+            pos = {i: n for n, i in enumerate(ids)}
+            for r in rows:
+                e = per.setdefault(pos[int(r["Dispatch_Id"])], {})
+                e[r["Counter_Name"]] = float(r["Counter_Value"])
+                e.setdefault("ns", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     if not per:
-        raise SystemExit("no fused-kernel dispatches in the counter run")
+        raise SystemExit(f"no {which} dispatches in the counter runs")
+    have = set.intersection(*(set(v) for v in per.values()))
     keys = sorted(per)
-    avg = {c: sum(per[k][c] for k in keys) / len(keys) for c in SQ_COUNTERS + ["ns"]}
+    avg = {c: sum(per[k][c] for k in keys) / len(keys) for c in have if c != "ns"}
+    avg["ns"] = sum(sum(per[k]["ns"]) / len(per[k]["ns"]) for k in keys) / len(keys)
     cycles = avg["SQ_BUSY_CYCLES"] / SHADER_ENGINES
     mhz = cycles / (avg["ns"] * 1e-3)
-    mfma_busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
-    flops = 4.0 * spec["B"] * spec["H"] * spec["N"] ** 2 * spec["d"]
-    tflops = flops / (avg["ns"] * 1e-9) / 1e12
-    peak_at_clock = PEAK_BF16_TFLOPS * mhz / 2400.0
-    waves = avg["SQ_WAVES"]
-    mfma = avg["SQ_INSTS_MFMA"]
+    _, flops_per_mfma, bench_args, tag = SQ_KERNELS[which]
     lines = [
-        f"# Shader counters of the fused forward, {spec['name']}",
+        f"# Shader counters of {which} ({SQ_KERNELS[which][0]}), {spec['name']}",
         "",
-        "Command (one MI355X, from the repository root):",
+        "Commands (one MI355X, from the repository root; one pass per counter set):",
         "",
         "```",
-        f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {pmc_dir} -o run --output-format csv -- "
-        f"python bench.py --workload {index} {SQ_BENCH_ARGS}",
-        f"python bench.py --workload {index} --sq-from {pmc_dir}",
-        "```",
-        "",
-        f"Averages over {len(keys)} dispatches of the fused kernel:",
-        "",
-        "| quantity | value |",
-        "|---|---|",
-        f"| dispatch duration | {avg['ns'] / 1e3:.1f} us ({tflops:.1f} TFLOP/s at 4BHN^2d) |",
-        f"| SQ_BUSY_CYCLES / 32 engines | {cycles:.0f} shader cycles |",
-        f"| effective shader clock | {mhz:.0f} MHz (nominal peak clock 2400 MHz) |",
-        f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / cycles) | {mfma_busy:.3f} |",
-        f"| dense bf16 MFMA peak at that clock | {peak_at_clock:.0f} TFLOP/s "
-        f"(achieved / that = {tflops / peak_at_clock:.3f}) |",
-        f"| waves | {waves:.0f} |",
-        f"| per wave: MFMA / VALU (incl. MFMA) / transcendental / LDS instructions | "
-        f"{mfma / waves:.0f} / {avg['SQ_INSTS_VALU'] / waves:.0f} / "
-        f"{avg['SQ_INSTS_VALU_TRANS_F32'] / waves:.0f} / {avg['SQ_INSTS_LDS'] / waves:.0f} |",
-        f"| non-MFMA VALU + LDS instructions per MFMA | "
-        f"{(avg['SQ_INSTS_VALU'] - mfma + avg['SQ_INSTS_LDS']) / mfma:.2f} |",
-        "",
-        f"kernel_sources_sha256_16: {sources_hash()}",
-        "",
     ]
-    path = os.path.join(ROOT, f"profiles/sq_counters_fused_fwd_{workload_tag(spec)}.md")
+    for name, d in zip(("a", "b"), pmc_dirs):
+        lines.append(f"rocprofv3 --pmc {' '.join(SQ_PASSES[name])} -d {d} -o run --output-format csv "
+                     f"-- python bench.py --workload {index} {bench_args}")
+    lines += [f"python bench.py --workload {index} --sq-kernel {which} --sq-from "
+              f"{' '.join(pmc_dirs)}", "```", "",
+              f"Averages over {len(keys)} dispatches:", "", "| quantity | value |", "|---|---|"]
+    mfma = avg.get("SQ_INSTS_MFMA")
+    tflops = mfma * flops_per_mfma / (avg["ns"] * 1e-9) / 1e12 if mfma else None
+    lines.append(f"| dispatch duration | {avg['ns'] / 1e3:.1f} us |")
+    if tflops:
+        lines.append(f"| executed MFMA rate (SQ_INSTS_MFMA x {flops_per_mfma:.0f} FLOP) | "
+                     f"{tflops:.1f} TFLOP/s |")
+    lines += [f"| SQ_BUSY_CYCLES / 32 engines | {cycles:.0f} shader cycles |",
+              f"| effective shader clock | {mhz:.0f} MHz (nominal peak clock 2400 MHz) |"]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
+        lines.append(f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / cycles) | {busy:.3f} |")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+        lines.append(f"| vector issue while MFMA busy (COEXEC / SIMDs / cycles) | "
+                     f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / (SIMDS * cycles):.3f} |")
+    if "SQ_ACTIVE_INST_VALU" in avg:
+        lines.append(f"| vector instructions active (4 x ACTIVE_INST_VALU / SIMDs / cycles) | "
+                     f"{4 * avg['SQ_ACTIVE_INST_VALU'] / (SIMDS * cycles):.3f} |")
+    if "SQ_ACTIVE_INST_LDS" in avg:
+        lines.append(f"| LDS instructions active (4 x ACTIVE_INST_LDS / SIMDs / cycles) | "
+                     f"{4 * avg['SQ_ACTIVE_INST_LDS'] / (SIMDS * cycles):.3f} |")
+    if "SQ_WAIT_ANY" in avg:
+        lines.append(f"| wave lifetime spent waiting (WAIT_ANY / WAVE_CYCLES) | "
+                     f"{avg['SQ_WAIT_ANY'] / avg['SQ_WAVE_CYCLES']:.3f} |")
+        lines.append(f"| wave lifetime waiting to issue LDS (WAIT_INST_LDS / WAVE_CYCLES) | "
+                     f"{avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.3f} |")
+    if "SQ_WAVES" in avg:
+        waves = avg["SQ_WAVES"]
+        lines.append(f"| waves | {waves:.0f} |")
+        lines.append(f"| per wave: MFMA / VALU (incl. MFMA) / transcendental / LDS instructions | "
+                     f"{mfma / waves:.0f} / {avg['SQ_INSTS_VALU'] / waves:.0f} / "
+                     f"{avg['SQ_INSTS_VALU_TRANS_F32'] / waves:.0f} / "
+                     f"{avg['SQ_INSTS_LDS'] / waves:.0f} |")
+        lines.append(f"| non-MFMA VALU + LDS instructions per MFMA | "
+                     f"{(avg['SQ_INSTS_VALU'] - mfma + avg['SQ_INSTS_LDS']) / mfma:.2f} |")
+        if "SQ_INSTS_SALU" in avg:
+            lines.append(f"| scalar instructions per wave | {avg['SQ_INSTS_SALU'] / waves:.0f} |")
+    lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"),
+                        f"sq_counters_{tag}_{workload_tag(spec)}.md")
     with open(path, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines))
     print(path)
+    return path
 
 
 def read_traffic(spec):
@@ -727,7 +775,7 @@ def main():
     args = parse()
     if args.sq_from:
         from workloads import WORKLOADS
-        summarise_sq(args.sq_from, args.workload, WORKLOADS[args.workload])
+        summarise_sq(args.sq_from, args.workload, WORKLOADS[args.workload], args.sq_kernel)
         return
     if args.trace_from:
         from workloads import WORKLOADS

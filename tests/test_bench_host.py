@@ -113,3 +113,49 @@ def test_trace_summary_without_the_profiled_run(tmp_path):
     text = open(bench.summarise_trace(str(trace), 3, WORKLOADS[3], "", out_dir=str(out))).read()
     assert "trace / events" not in text
     assert bench.BENCH_STDOUT not in text
+
+
+def _pmc_csv(directory, kernel, grid, values, ns, dispatches=3):
+    import csv
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                           "Counter_Name", "Counter_Value", "Start_Timestamp",
+                                           "End_Timestamp"])
+        w.writeheader()
+        for i in range(dispatches):
+            for c, v in values.items():
+                w.writerow({"Dispatch_Id": 10 + 2 * i, "Kernel_Name": kernel, "Grid_Size": grid,
+                            "Counter_Name": c, "Counter_Value": v, "Start_Timestamp": 1000,
+                            "End_Timestamp": 1000 + ns})
+
+
+def test_shader_counter_summary_of_two_passes(tmp_path):
+    # a kernel of 200 us at 1500 MHz: 300000 cycles per engine; MFMA busy
+    # half the SIMD-cycles; waves wait a quarter of their lifetime
+    cyc = 300000.0
+    a = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * bench.SIMDS * cyc,
+         "SQ_INSTS_VALU": 6000.0 * 4096, "SQ_INSTS_MFMA": 1000.0 * 4096, "SQ_INSTS_LDS": 500.0 * 4096,
+         "SQ_INSTS_VALU_TRANS_F32": 900.0 * 4096, "SQ_WAVES": 4096.0, "SQ_WAVE_CYCLES": 4.0e8}
+    b = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_WAVE_CYCLES": 4.0e8, "SQ_WAIT_ANY": 1.0e8,
+         "SQ_WAIT_INST_LDS": 2.0e7, "SQ_VALU_MFMA_COEXEC_CYCLES": 0.2 * bench.SIMDS * cyc,
+         "SQ_ACTIVE_INST_VALU": 0.1 * bench.SIMDS * cyc, "SQ_ACTIVE_INST_LDS": 0.05 * bench.SIMDS * cyc,
+         "SQ_INSTS_SALU": 100.0 * 4096}
+    name = "void iofa::bwd_dkdv_kernel<iofa::Bf16, 128>(...)"
+    _pmc_csv(str(tmp_path / "a"), name, 1024, a, 200000)
+    _pmc_csv(str(tmp_path / "b"), name, 1024, b, 200000)
+    out = tmp_path / "out"
+    out.mkdir()
+    path = bench.summarise_sq([str(tmp_path / "a"), str(tmp_path / "b")], 3, WORKLOADS[3],
+                              "bwd_dkdv", out_dir=str(out))
+    text = open(path).read()
+    assert os.path.basename(path) == "sq_counters_bwd_dkdv_bf16_B2H16N4096d128.md"
+    assert "| effective shader clock | 1500 MHz" in text
+    assert "| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs / cycles) | 0.500 |" in text
+    assert "(COEXEC / SIMDs / cycles) | 0.200 |" in text
+    assert "(4 x ACTIVE_INST_VALU / SIMDs / cycles) | 0.400 |" in text
+    assert "(WAIT_ANY / WAVE_CYCLES) | 0.250 |" in text
+    assert "(WAIT_INST_LDS / WAVE_CYCLES) | 0.050 |" in text
+    assert "| 1000 / 6000 / 900 / 500 |" in text
+    # 1000 MFMAs per wave x 4096 waves x 32768 FLOP in 200 us
+    assert f"{1000 * 4096 * 32768 / 200e-6 / 1e12:.1f} TFLOP/s" in text
