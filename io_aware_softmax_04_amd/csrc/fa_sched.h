@@ -25,6 +25,31 @@ __device__ inline void interleave_mfma_valu() {
   interleave_step<NMFMA, NDS - LEAD, VPM, 0>();
 }
 
+// The same with the reads kept LEAD ahead of their consumers for the whole
+// region: the products consume the NDS reads about evenly (NDS / NMFMA
+// each), and before product k the reads issued are
+// min(NDS, LEAD + ceil(k NDS / NMFMA)).  With interleave_mfma_valu the lead
+// drains to nothing by the region's last products when NDS > NMFMA.
+template <int NMFMA, int NDS, int LEAD, int VPM, int I>
+__device__ inline void interleave_lead_step() {
+  if constexpr (I < NMFMA) {
+    constexpr auto issued = [](int k) {
+      const int c = (k * NDS + NMFMA - 1) / NMFMA + LEAD;
+      return c < NDS ? c : NDS;
+    };
+    constexpr int nrd = issued(I + 1) - issued(I);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    if constexpr (nrd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nrd, 0);   // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);       // VALU
+    interleave_lead_step<NMFMA, NDS, LEAD, VPM, I + 1>();
+  }
+}
+template <int NMFMA, int NDS, int LEAD, int VPM>
+__device__ inline void interleave_mfma_valu_lead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD < NDS ? LEAD : NDS, 0);   // DS reads
+  interleave_lead_step<NMFMA, NDS, LEAD, VPM, 0>();
+}
+
 // Position of a workgroup in the grid.  The logical order (contiguous per
 // XCD, see xcd_logical_id) is ((bh * splits) + split) * qtiles + qt, so the
 // query tiles of one head and key range run side by side on one XCD and
