@@ -319,16 +319,17 @@ SQ_PASSES = {
 SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
 SIMDS = 1024                 # 256 CUs x 4
 # Kernels the counter summary covers: (name filter, FLOPs per MFMA instruction,
-# bench.py arguments of the counter passes, file tag)
+# bench.py arguments of the counter passes, file tag, rocprofv3 kernel regex)
+_SQ_COMMON = "--warmup 100 --no-naive --no-splitkv --no-softmax --no-ceiling --no-cpu-baseline"
 SQ_KERNELS = {
-    "fused": ("fused", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax --no-backward "
-              "--no-fp8 --no-ceiling --no-cpu-baseline", "fused_fwd"),
-    "bwd_dq": ("bwd_dq_kernel", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
-               "--no-fp8 --no-ceiling --no-cpu-baseline", "bwd_dq"),
-    "bwd_dkdv": ("bwd_dkdv_kernel", 32768.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
-                 "--no-fp8 --no-ceiling --no-cpu-baseline", "bwd_dkdv"),
-    "fp8": ("fa_fwd_fp8_kernel", 131072.0, "--steps 20 --no-naive --no-splitkv --no-softmax "
-            "--no-backward --no-ceiling --no-cpu-baseline", "fp8_fwd"),
+    "fused": ("fused", 32768.0, f"--steps 20 {_SQ_COMMON} --no-backward --no-fp8", "fused_fwd",
+              "fa_fwd_16_kernel"),
+    "bwd_dq": ("bwd_dq_kernel", 32768.0, f"--steps 20 {_SQ_COMMON} --no-fp8", "bwd_dq",
+               "bwd_dq_kernel"),
+    "bwd_dkdv": ("bwd_dkdv_kernel", 32768.0, f"--steps 20 {_SQ_COMMON} --no-fp8", "bwd_dkdv",
+                 "bwd_dkdv_kernel"),
+    "fp8": ("fa_fwd_fp8_kernel", 131072.0, f"--steps 20 {_SQ_COMMON} --no-backward", "fp8_fwd",
+            "fa_fwd_fp8_kernel"),
 }
 
 
@@ -371,13 +372,18 @@ def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
                 e.setdefault("ns", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     if not per:
         raise SystemExit(f"no {which} dispatches in the counter runs")
-    have = set.intersection(*(set(v) for v in per.values()))
+    # each counter is averaged over the dispatches that carry it (the passes
+    # need not hold the same number of dispatches)
     keys = sorted(per)
-    avg = {c: sum(per[k][c] for k in keys) / len(keys) for c in have if c != "ns"}
+    names = set().union(*(set(v) for v in per.values())) - {"ns"}
+    avg = {}
+    for c in names:
+        vals = [per[k][c] for k in keys if c in per[k]]
+        avg[c] = sum(vals) / len(vals)
     avg["ns"] = sum(sum(per[k]["ns"]) / len(per[k]["ns"]) for k in keys) / len(keys)
     cycles = avg["SQ_BUSY_CYCLES"] / SHADER_ENGINES
     mhz = cycles / (avg["ns"] * 1e-3)
-    _, flops_per_mfma, bench_args, tag = SQ_KERNELS[which]
+    _, flops_per_mfma, bench_args, tag, regex = SQ_KERNELS[which]
     lines = [
         f"# Shader counters of {which} ({SQ_KERNELS[which][0]}), {spec['name']}",
         "",
@@ -386,7 +392,8 @@ def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
         "```",
     ]
     for name, d in zip(("a", "b"), pmc_dirs):
-        lines.append(f"rocprofv3 --pmc {' '.join(SQ_PASSES[name])} -d {d} -o run --output-format csv "
+        lines.append(f"rocprofv3 --pmc {' '.join(SQ_PASSES[name])} --kernel-include-regex "
+                     f"'{regex}' -d {d} -o run --output-format csv "
                      f"-- python bench.py --workload {index} {bench_args}")
     lines += [f"python bench.py --workload {index} --sq-kernel {which} --sq-from "
               f"{' '.join(pmc_dirs)}", "```", "",

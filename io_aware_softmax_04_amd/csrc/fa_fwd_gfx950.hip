@@ -390,10 +390,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     vcp.copy(Vh, j * BC, NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv_scores<1 - P, 1 - P>(p_prev, s_nxt);
-    // d = 128 keeps its reads LEAD ahead for the whole tile; at d = 64 the
-    // draining order measured faster (21.0 vs 21.7 us at B4 H16 N1024)
+    // d = 128 keeps its reads LEAD ahead for the whole tile, with three
+    // vector instructions per product (four: 1.1-1.5% slower at B2 H16
+    // N4096, B2 H8 N8191 and B1 H32 N16384; two: 0.5% slower); at d = 64 the
+    // draining order with four measured faster (21.0 vs 21.7 us at
+    // B4 H16 N1024)
     if constexpr (D == 128)
-      interleave_mfma_valu_lead<NM, NRD, LEAD, 4>();
+      interleave_mfma_valu_lead<NM, NRD, LEAD, 3>();
     else
       interleave_mfma_valu<NM, NRD, LEAD, 4>();
     // the redo decision is wave-uniform, so the accepted path (almost every

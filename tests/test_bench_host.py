@@ -159,3 +159,24 @@ def test_shader_counter_summary_of_two_passes(tmp_path):
     assert "| 1000 / 6000 / 900 / 500 |" in text
     # 1000 MFMAs per wave x 4096 waves x 32768 FLOP in 200 us
     assert f"{1000 * 4096 * 32768 / 200e-6 / 1e12:.1f} TFLOP/s" in text
+
+
+def test_shader_counter_summary_with_unequal_passes(tmp_path):
+    # pass a has 3 dispatches, pass b 5: each counter averages its own
+    cyc = 300000.0
+    a = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.4 * bench.SIMDS * cyc,
+         "SQ_INSTS_VALU": 100.0, "SQ_INSTS_MFMA": 10.0, "SQ_INSTS_LDS": 5.0,
+         "SQ_INSTS_VALU_TRANS_F32": 1.0, "SQ_WAVES": 1.0, "SQ_WAVE_CYCLES": 1.0e8}
+    b = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_WAVE_CYCLES": 1.0e8, "SQ_WAIT_ANY": 3.0e7,
+         "SQ_WAIT_INST_LDS": 1.0e7, "SQ_VALU_MFMA_COEXEC_CYCLES": 0.1 * bench.SIMDS * cyc,
+         "SQ_ACTIVE_INST_VALU": 0.1 * bench.SIMDS * cyc,
+         "SQ_ACTIVE_INST_LDS": 0.1 * bench.SIMDS * cyc, "SQ_INSTS_SALU": 7.0}
+    name = "void iofa::(anonymous namespace)::fa_fwd_fp8_kernel<128>(...)"
+    _pmc_csv(str(tmp_path / "a"), name, 1024, a, 150000, dispatches=3)
+    _pmc_csv(str(tmp_path / "b"), name, 1024, b, 150000, dispatches=5)
+    out = tmp_path / "out"
+    out.mkdir()
+    text = open(bench.summarise_sq([str(tmp_path / "a"), str(tmp_path / "b")], 3, WORKLOADS[3],
+                                   "fp8", out_dir=str(out))).read()
+    assert "| 0.400 |" in text and "(WAIT_ANY / WAVE_CYCLES) | 0.300 |" in text
+    assert "| 10 / 100 / 1 / 5 |" in text
