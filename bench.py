@@ -139,10 +139,13 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
         copy = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL_NAME in r["Kernel_Name"]]
         if not fused or not copy:
             raise SystemExit(f"{counter}: fused or calibration-copy dispatches missing")
-        factor = copy_bytes / (sum(copy) / len(copy) * 1024)
+        # the runtime may run the one calibration copy as several dispatches:
+        # their counts add up (other copies in the run are a few KiB)
+        factor = copy_bytes / (sum(copy) * 1024)
         kib = sum(fused) / len(fused)
         out[counter] = dict(kib=kib, factor=factor, bytes=kib * 1024 * factor,
-                            dispatches=len(fused), copy_kib=sum(copy) / len(copy))
+                            dispatches=len(fused), copy_kib=sum(copy),
+                            copy_dispatches=len(copy))
     total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
     # the naive contrast's three kernels, if the runs included them
     naive = {}
@@ -168,7 +171,9 @@ def summarise_traffic(fetch_dir, write_dir, copy_mib, index, spec):
         f"{fetch_dir} {write_dir} --copy-mib {copy_mib}",
         "```",
         "",
-        f"Calibration: a device copy of {copy_mib} MiB ({COPY_KERNEL_NAME}) reads "
+        f"Calibration: a device copy of {copy_mib} MiB ({COPY_KERNEL_NAME}, "
+        f"{out['FETCH_SIZE']['copy_dispatches']} and {out['WRITE_SIZE']['copy_dispatches']} "
+        f"dispatches of that kernel in the two runs, counts summed) reads "
         f"{out['FETCH_SIZE']['copy_kib']:.1f} KiB on FETCH_SIZE and writes "
         f"{out['WRITE_SIZE']['copy_kib']:.1f} KiB on WRITE_SIZE, so the counters are "
         f"scaled by {out['FETCH_SIZE']['factor']:.4f} (fetch) and "

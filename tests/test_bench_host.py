@@ -180,3 +180,48 @@ def test_shader_counter_summary_with_unequal_passes(tmp_path):
                                    "fp8", out_dir=str(out))).read()
     assert "| 0.400 |" in text and "(WAIT_ANY / WAVE_CYCLES) | 0.300 |" in text
     assert "| 10 / 100 / 1 / 5 |" in text
+
+
+def test_traffic_calibration_sums_a_split_copy(tmp_path):
+    # the 1024 MiB calibration copy ran as two dispatches of 512 MiB: the
+    # scale comes from their sum, not their mean
+    import csv
+
+    def pmc(directory, counter, fused_kib, copy_kibs):
+        os.makedirs(directory)
+        with open(os.path.join(directory, "run_counter_collection.csv"), "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                               "Counter_Name", "Counter_Value",
+                                               "Start_Timestamp", "End_Timestamp"])
+            w.writeheader()
+            n = 0
+            for v in copy_kibs:
+                w.writerow({"Dispatch_Id": n, "Kernel_Name": bench.COPY_KERNEL_NAME, "Grid_Size": 512,
+                            "Counter_Name": counter, "Counter_Value": v, "Start_Timestamp": 0,
+                            "End_Timestamp": 1})
+                n += 1
+            for _ in range(3):
+                w.writerow({"Dispatch_Id": n, "Grid_Size": bench.fused_grid_items(WORKLOADS[3]),
+                            "Kernel_Name": "void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false>()",
+                            "Counter_Name": counter, "Counter_Value": fused_kib,
+                            "Start_Timestamp": 0, "End_Timestamp": 1})
+                n += 1
+
+    # FETCH_SIZE sees half the bytes read, WRITE_SIZE all the bytes written
+    pmc(str(tmp_path / "f"), "FETCH_SIZE", 49260.0, [262144.0, 262144.0])
+    pmc(str(tmp_path / "w"), "WRITE_SIZE", 33280.0, [524288.0, 524288.0])
+    old = bench.ROOT
+    try:
+        bench.ROOT = str(tmp_path)
+        os.makedirs(tmp_path / "profiles")
+        os.makedirs(tmp_path / "io_aware_softmax_04_amd" / "csrc")
+        for rel in bench.FUSED_KERNEL_SOURCES:
+            open(tmp_path / rel, "w").write("x")
+        bench.summarise_traffic(str(tmp_path / "f"), str(tmp_path / "w"), 1024, 3, WORKLOADS[3])
+        text = open(tmp_path / "profiles" / "traffic_fused_fwd_bf16_B2H16N4096d128.md").read()
+    finally:
+        bench.ROOT = old
+    assert "scaled by 2.0000 (fetch) and 4.0000 (write)" not in text
+    assert "scaled by 4.0000 (fetch) and 2.0000 (write)" not in text
+    assert "scaled by 2.0000 (fetch) and 1.0000 (write)" in text
+    assert f"bytes_per_launch: {round(49260.0 * 1024 * 2 + 33280.0 * 1024)}" in text
