@@ -752,12 +752,13 @@ def ceiling_cases(lines):
 
 
 def softmax_measure(args, torch, iofa, dev):
-    """The standalone row softmax on bf16 rows that fit one workgroup (x read
-    once, y written once) and on long rows (x read twice).  Roofline: HBM;
+    """The standalone row softmax on bf16 rows that fit one workgroup, on
+    rows of 4 slices (the one-pass resident form) and on rows of 256 slices
+    (two passes: x read twice), 512 MiB of x each.  Roofline: HBM;
     algorithmic bytes = read x once + write y once + 4 bytes of LSE per
-    row."""
+    row; x_reads is what the library reports for the call."""
     out = []
-    for rows, n in ((32768, 8192), (64, 1 << 22)):
+    for rows, n in ((32768, 8192), (4096, 1 << 16), (64, 1 << 22)):
         g = torch.Generator(device=dev).manual_seed(rows)
         x = (torch.randn((rows, n), generator=g, device=dev) * 4).to(torch.bfloat16)
         y = torch.empty_like(x)
@@ -765,10 +766,10 @@ def softmax_measure(args, torch, iofa, dev):
         nb = iofa.fa_softmax_workspace_bytes(rows, n, x.dtype)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
         steps = max(5, min(args.steps, 30))
-        _, ms, *_ = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
-                              steps, 3, torch, warm_seconds=0.3)
+        wall, ms, *_ = time_launches(lambda: iofa.fa_softmax_rows(x, y, lse, ws if nb else None),
+                                     steps, 3, torch, warm_seconds=0.3)
         alg = rows * n * 2 * 2 + rows * 4
-        reads = 1 if nb == 0 else 2
+        reads = iofa.fa_softmax_x_reads(x, y)
         moved = rows * n * 2 * (reads + 1) + rows * 4
         gbs = alg / (ms * 1e-3) / 1e9
         out.append({
@@ -778,6 +779,10 @@ def softmax_measure(args, torch, iofa, dev):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes": alg},
             "moved_bytes_per_s_GBs": round(moved / (ms * 1e-3) / 1e9, 1),
+            # calls back to back (no event between them): the rate a stream
+            # of calls sees; a multi-kernel call loses its launch gaps there
+            "ms_back_to_back": round(wall, 4),
+            "frac_back_to_back": round(alg / (wall * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         })
         del x, y, ws
     return out

@@ -234,30 +234,56 @@ int fa_merge_partials(const float* O_part, const float* LSE_part, int num_parts,
  * l_r = sum_j e^{X[r, j] - m_r}; LSE[r] = m_r + ln l_r.  The online softmax
  * of xinc.fun archive 235, section "7. Online Softmax" (a running maximum and
  * denominator, the old denominator rescaled by e^{m_old - m_new} when a
- * block raises the maximum), as a memory-bound operation of its own:
- *   rows of at most 8192 (16-bit) / 4096 (fp32) elements are read once and
- *   written once; longer rows are cut into chunks of that size whose
- *   (m, l) pairs are combined with the block merge of the
- *   special-jiahao.github.io "Flash Attention" note ("增量求解 softmax"),
- *   reading X twice (the three-pass maximum / sum / normalise form reads it
- *   three times).
+ * block raises the maximum), as a memory-bound operation of its own.  Rows
+ * are cut into pieces whose (m, l) pairs are combined with the block merge
+ * of the special-jiahao.github.io "Flash Attention" note ("增量求解 softmax"):
+ *   rows of at most 8192 (16-bit) / 4096 (fp32) elements: one workgroup per
+ *     row; X read once, Y written once;
+ *   rows of at most 32 slices of 16384 (16-bit) / 8192 (fp32) elements whose
+ *     length keeps them 16-byte aligned, with X and Y 16-byte aligned: one
+ *     workgroup per slice holds it in registers until the row's pairs are
+ *     merged (X read once), provided the device can hold that many
+ *     workgroups at once;
+ *   other rows: the pairs of 8192 / 4096-element chunks are merged per row
+ *     between two passes (X read twice).
+ * The three-pass maximum / sum / normalise form reads X three times;
+ * fa_softmax_x_reads() tells which form a call takes.
  *   X    in:  (rows, n) contiguous, `dtype`, element-aligned (rows of a
  *             length that keeps them 16-byte aligned use 16-byte accesses).
  *   Y    out: (rows, n) contiguous, `dtype` (RNE); may equal X (in place),
  *             must not otherwise overlap it.
  *   LSE  out: (rows) fp32, or NULL.
  *   workspace  caller-owned device memory of fa_softmax_workspace_bytes()
- *             bytes, 8-byte aligned; NULL allowed when that size is 0.
- * Arithmetic is fp32 for every dtype.  rows or n equal to 0: nothing is
- * enqueued.  Errors as fa_fwd.
+ *             bytes, 8-byte aligned; NULL allowed when that size is 0.  Its
+ *             contents need no initialisation; calls sharing one workspace
+ *             must be ordered (one stream, or synchronised streams).
+ * Arithmetic is fp32 for every dtype.  The one-pass slice form waits inside
+ * a kernel for the other slices of a row; each wait is bounded, and slices
+ * whose wait ran out are written by a further kernel of the same call, so
+ * the result never depends on how many workgroups ran at once.  rows or n
+ * equal to 0: nothing is enqueued.  Errors as fa_fwd.
  */
 int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_softmax_rows needs: rows * chunks * 8 for rows longer
- * than one chunk, else 0 (also for invalid arguments and sizes that do not
- * fit size_t). */
+/* Workspace bytes fa_softmax_rows needs: for rows longer than one chunk the
+ * larger of rows * (chunks + 1) * 8 (two passes: chunk pairs and row pairs)
+ * and 16 + 12 * rows * slices (one pass: counters, slice pairs and flags),
+ * else 0 (also for invalid arguments and sizes that do not fit size_t). */
 size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype);
+
+/* How many times fa_softmax_rows with these arguments would read X from
+ * memory on the current device: 1 (one-chunk rows, slice-resident rows) or
+ * 2 (two passes); 0 for invalid arguments.  X and Y only matter through
+ * their 16-byte alignment; nothing is dereferenced or enqueued. */
+int fa_softmax_x_reads(const void* X, const void* Y, int64_t rows, int64_t n, int dtype);
+
+/* Diagnostics: sets the number of polls after which a slice of the one-pass
+ * form stops waiting for the rest of its row and leaves itself to the repair
+ * kernel (default 400, about half a millisecond; 0 gives up after one poll,
+ * which exercises the repair path; negative restores the default).  Returns
+ * the previous setting.  Process-wide; results do not depend on it. */
+int fa_softmax_set_wait_limit(int polls);
 
 /*
  * Backward pass of exact attention: dQ, dK, dV for an upstream gradient dO

@@ -3,7 +3,7 @@
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_fwd_splitkv_noalloc``,
 ``fa_splitkv_num_splits``,
 ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
-``fa_softmax_workspace_bytes``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_fp8``,
+``fa_softmax_workspace_bytes``, ``fa_softmax_x_reads``, ``fa_softmax_set_wait_limit``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_fp8``,
 ``fa_naive_fwd``,
 ``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
 ``fa_version`` carry the names
@@ -28,7 +28,8 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
     "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
-    "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "softmax",
+    "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_softmax_x_reads",
+    "fa_softmax_set_wait_limit", "softmax",
     "fa_bwd", "fa_bwd_workspace_bytes", "backward", "fa_fwd_fp8", "forward_fp8",
     "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string",
     "fa_last_error", "fa_version", "forward", "forward_splitkv", "naive_forward",
@@ -88,6 +89,10 @@ def load_library():
     lib.fa_softmax_rows.restype = ctypes.c_int
     lib.fa_softmax_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
     lib.fa_softmax_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_softmax_x_reads.argtypes = [vp, vp, i64, i64, ctypes.c_int]
+    lib.fa_softmax_x_reads.restype = ctypes.c_int
+    lib.fa_softmax_set_wait_limit.argtypes = [ctypes.c_int]
+    lib.fa_softmax_set_wait_limit.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, vp, ctypes.c_size_t,
                            i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
@@ -291,6 +296,23 @@ def fa_softmax_rows(x, y, lse=None, workspace=None, stream=None):
 def fa_softmax_workspace_bytes(rows, n, dtype):
     code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load_library().fa_softmax_workspace_bytes(rows, n, code))
+
+
+def fa_softmax_x_reads(x, y=None):
+    """How many times fa_softmax_rows(x, y) would read x from memory on the
+    current device (1 or 2); y defaults to x (in place)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    y = x if y is None else y
+    return int(load_library().fa_softmax_x_reads(_ptr(x), _ptr(y), x.shape[0], x.shape[1],
+                                                 _DTYPE_CODE[x.dtype]))
+
+
+def fa_softmax_set_wait_limit(polls):
+    """Diagnostics: the one-pass softmax's bound on each wait, in polls (0
+    sends every slice that finds its row incomplete to the repair kernel;
+    negative restores the default).  Returns the previous bound."""
+    return int(load_library().fa_softmax_set_wait_limit(int(polls)))
 
 
 def softmax(x, want_lse=False, stream=None):

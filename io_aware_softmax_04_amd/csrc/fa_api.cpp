@@ -4,6 +4,7 @@
 // without a GPU.
 #include "../../include/fa_api.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <initializer_list>
@@ -326,8 +327,14 @@ size_t fa_softmax_workspace_bytes(int64_t rows, int64_t n, int dtype) {
   if (elem_bytes(dtype) == 0 || rows < 0 || n < 0) return 0;
   const int64_t chunk = iofa::softmax_chunk(dtype);
   if (n <= chunk) return 0;
-  return product_or_zero({static_cast<size_t>(rows), static_cast<size_t>(ceil_div(n, chunk)),
-                          2 * sizeof(float)});
+  // two passes: a pair per chunk, then one per row
+  const size_t two = product_or_zero({static_cast<size_t>(rows), static_cast<size_t>(ceil_div(n, chunk)) + 1,
+                                      2 * sizeof(float)});
+  // one pass: two counters, then a pair (8 bytes) and a flag (4) per slice
+  const size_t one = product_or_zero({static_cast<size_t>(rows),
+                                      static_cast<size_t>(ceil_div(n, iofa::softmax_slice(dtype))), 12});
+  if (two == 0 || one == 0 || one > SIZE_MAX - 16) return 0;
+  return std::max(two, one + 16);
 }
 
 int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n, int dtype,
@@ -339,8 +346,8 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
   if (rows < 0 || n < 0) return fail(FA_ERR_SHAPE, "rows and n must be >= 0");
   if (rows == 0 || n == 0) return FA_OK;
   const int64_t chunk = iofa::softmax_chunk(dtype);
-  const int64_t chunks = ceil_div(n, chunk);
-  if (chunks > INT32_MAX || rows > INT32_MAX / chunks)   // rows * chunks < 2^31
+  const int64_t pieces = ceil_div(n, iofa::softmax_piece(dtype));   // the largest grid per row
+  if (pieces > INT32_MAX || rows > INT32_MAX / pieces)   // rows * pieces < 2^31
     return fail(FA_ERR_SHAPE, "too many workgroups");
   if (!X || !Y) return fail(FA_ERR_NULL, "X and Y must not be NULL");
   if (!aligned(X, e) || !aligned(Y, e)) return fail(FA_ERR_ALIGN, "X and Y must be element-aligned");
@@ -354,7 +361,7 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
       return fail(FA_ERR_SHAPE, "workspace holds " + std::to_string(workspace_bytes) +
                                     " bytes, rows of this length need " + std::to_string(need));
   }
-  // Y == X (in place) is allowed: every workgroup reads its chunk in full
+  // Y == X (in place) is allowed: every workgroup reads its piece in full
   // before writing it, and pass 2 starts after pass 1.  Partial overlap is not.
   const size_t bytes = static_cast<size_t>(rows) * static_cast<size_t>(n) * e;
   const Region in[1] = {{X, Y == X ? 0 : bytes, "X"}};
@@ -369,6 +376,14 @@ int fa_softmax_rows(const void* X, void* Y, float* LSE, int64_t rows, int64_t n,
   iofa::SoftmaxArgs a{X, Y, LSE, rows, n, dtype, workspace, static_cast<hipStream_t>(stream)};
   return hip_status(iofa::launch_softmax(a), "softmax launch");
 }
+
+int fa_softmax_x_reads(const void* X, const void* Y, int64_t rows, int64_t n, int dtype) {
+  if (elem_bytes(dtype) == 0 || rows <= 0 || n <= 0) return 0;
+  const iofa::SoftmaxArgs a{X, const_cast<void*>(Y), nullptr, rows, n, dtype, nullptr, nullptr};
+  return iofa::softmax_x_reads(a);
+}
+
+int fa_softmax_set_wait_limit(int polls) { return iofa::softmax_wait_limit(polls); }
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B < 0 || H < 0 || N < 0) return 0;

@@ -48,8 +48,9 @@ struct MergeArgs {
   hipStream_t stream;
 };
 
-// Row softmax of X (rows, n) into Y; workspace: rows * chunks float2 (m, l)
-// pairs for rows longer than one chunk.
+// Row softmax of X (rows, n) into Y.  Workspace for rows longer than one
+// chunk: the two-pass form uses rows * (chunks + 1) float2 (m, l) pairs, the
+// resident form 16 + 12 * rows * parts bytes (parts = slices per row).
 struct SoftmaxArgs {
   const void* X;
   void* Y;
@@ -60,9 +61,19 @@ struct SoftmaxArgs {
   void* workspace;
   hipStream_t stream;
 };
-// Elements of a row one workgroup covers.
+// Elements of a row one workgroup covers in the one-chunk form and in pass 1.
 int64_t softmax_chunk(int dtype);
+// Elements of one slice (task) of the resident form.
+int64_t softmax_slice(int dtype);
+// Elements one workgroup of pass 2 covers on 16-byte-aligned rows (the
+// smallest piece any launch uses).
+int64_t softmax_piece(int dtype);
 hipError_t launch_softmax(const SoftmaxArgs& a);
+// How many times launch_softmax(a) reads X from memory (1 or 2).
+int softmax_x_reads(const SoftmaxArgs& a);
+// Sets the resident form's bound on each wait (polls; negative restores the
+// default) and returns the previous bound.
+int softmax_wait_limit(int polls);
 
 // Backward pass (16-bit inputs): dQ, dK, dV from Q, K, V, O, dO and the
 // forward's LSE; stats: B*H*N float2 workspace of (LSE * log2 e, D).

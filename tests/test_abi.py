@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_splitkv_num_splits",
         "fa_splitkv_workspace_bytes",
-        "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_bwd",
+        "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes",
+        "fa_softmax_x_reads", "fa_softmax_set_wait_limit", "fa_bwd",
         "fa_bwd_workspace_bytes", "fa_fwd_fp8", "fa_naive_fwd",
         "fa_naive_workspace_bytes", "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -220,10 +221,31 @@ def softmax_call(lib, x=Q, y=O, lse=L, rows=4, n=100000, dtype=2, ws=WS, ws_byte
 
 
 def test_softmax_workspace_bytes(lib):
+    # the larger of (chunks + 1) pairs per row (two passes) and 16 bytes of
+    # counters plus 12 bytes per slice (one pass)
     assert iofa.fa_softmax_workspace_bytes(10, 8192, 2) == 0          # one chunk
-    assert iofa.fa_softmax_workspace_bytes(10, 8193, 2) == 10 * 2 * 8
-    assert iofa.fa_softmax_workspace_bytes(3, 1 << 20, 0) == 3 * 256 * 8   # fp32 chunk 4096
+    assert iofa.fa_softmax_workspace_bytes(10, 8193, 2) == 10 * 3 * 8
+    assert iofa.fa_softmax_workspace_bytes(1, 8193, 2) == 16 + 12     # one slice
+    assert iofa.fa_softmax_workspace_bytes(3, 1 << 20, 0) == 3 * 257 * 8   # fp32 chunk 4096
+    assert iofa.fa_softmax_workspace_bytes(64, 1 << 22, 2) == 64 * 513 * 8
     assert iofa.fa_softmax_workspace_bytes(3, 100, 7) == 0
+    assert iofa.fa_softmax_workspace_bytes(-1, 100000, 2) == 0
+
+
+def test_softmax_x_reads_and_wait_limit(lib):
+    f = lib.fa_softmax_x_reads
+    vp = ctypes.c_void_p
+    assert f(vp(Q), vp(O), 4, 8192, 2) == 1            # one chunk: always one read
+    assert f(vp(Q), vp(O), 4, 4096, 0) == 1
+    assert f(vp(Q), vp(O), 4, 1 << 22, 2) == 2         # 256 slices: two passes
+    assert f(vp(Q + 2), vp(O), 4, 100000, 2) == 2      # not 16-byte aligned: two passes
+    assert f(vp(Q), vp(O), 4, 100001, 2) == 2          # odd length: two passes
+    assert f(vp(Q), vp(O), 4, 100000, 2) in (1, 2)     # one pass where the device allows
+    assert f(vp(Q), vp(O), 0, 100000, 2) == 0
+    assert f(vp(Q), vp(O), 4, 100000, 9) == 0
+    prev = lib.fa_softmax_set_wait_limit(5)
+    assert lib.fa_softmax_set_wait_limit(-1) == 5
+    assert lib.fa_softmax_set_wait_limit(prev) == prev == 400
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -61,7 +61,13 @@ def _check(x, y, lse, label):
         assert np.all(d <= rel * (1 + np.abs(lse_ref))), f"{label}: lse {d.max():.3e}"
 
 
-SHAPES = [(1, 1), (3, 7), (5, 100), (7, 4096), (4, 8192), (4, 8193), (2, 20001), (3, 1 << 18)]
+# One-chunk rows, rows that take the two passes (odd lengths: scalar
+# accesses; aligned rows of more than 32 slices: 16-byte accesses) and rows
+# of at most 32 slices that take the one-pass resident form, with ragged last
+# slices (16392 = 2 slices + 8 elements for 16-bit types) and the 32-slice
+# boundary ((1 << 19) 16-bit elements are 32 slices, 16 more are 33).
+SHAPES = [(1, 1), (3, 7), (5, 100), (7, 4096), (4, 8192), (4, 8193), (2, 20001), (2, 8200),
+          (5, 16392), (3, 40000), (3, 1 << 18), (2, 1 << 19), (2, (1 << 19) + 16), (2, 1 << 20)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
@@ -76,7 +82,8 @@ def test_softmax_matches_oracle(dtype, dev):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_softmax_in_place_and_rows_sum_to_one(dtype, dev):
-    for rows, n in ((6, 3000), (3, 50000)):
+    # one chunk, one-pass slices, two passes with 16-byte and with scalar accesses
+    for rows, n in ((6, 3000), (3, 50000), (2, 1 << 20), (3, 20001)):
         x = _inputs(rows, n, dtype, seed=n)
         xd = x.to(dev)
         nbytes = iofa.fa_softmax_workspace_bytes(rows, n, xd.dtype)
@@ -86,6 +93,46 @@ def test_softmax_in_place_and_rows_sum_to_one(dtype, dev):
         _check(x, xd, None, f"in place {dtype} {rows}x{n}")
         s = xd.double().sum(dim=1).cpu().numpy()
         assert np.abs(s - 1).max() <= (2e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_softmax_forms_cover_every_path(dev):
+    # which form the shapes above take on an idle device (the one-pass form
+    # needs its grid resident at once, which an MI355X allows for 32 slices)
+    def reads(rows, n, dtype):
+        x = torch.empty((rows, n), dtype=DT[dtype], device=dev)
+        return iofa.fa_softmax_x_reads(x, torch.empty_like(x))
+    assert reads(7, 4096, "bf16") == 1
+    assert reads(4, 8193, "bf16") == 2            # odd length: scalar two passes
+    assert reads(2, 8200, "bf16") == 1
+    assert reads(5, 16392, "fp32") == 1
+    assert reads(3, 1 << 18, "bf16") == 1
+    assert reads(2, 1 << 19, "bf16") == 1         # 32 slices
+    assert reads(2, (1 << 19) + 16, "bf16") == 2  # 33 slices
+    assert reads(2, 1 << 19, "fp32") == 2         # 64 slices of 8192
+    assert reads(64, 1 << 22, "bf16") == 2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_softmax_repair_path_matches_oracle(dtype, dev):
+    # a wait bound of one poll sends every slice that finds its row
+    # incomplete to the repair kernel; the results must not change
+    prev = iofa.fa_softmax_set_wait_limit(0)
+    try:
+        for rows, n in ((3, 1 << 18), (5, 16392), (40, 100000)):
+            x = _inputs(rows, n, dtype, seed=3 * rows + n)
+            print(f"softmax repair {dtype} rows={rows} n={n}", flush=True)
+            y, lse = iofa.softmax(x.to(dev), want_lse=True)
+            torch.cuda.synchronize()
+            _check(x, y, lse, f"repair {dtype} {rows}x{n}")
+        x = _inputs(3, 50000, dtype, seed=17)
+        xd = x.to(dev)
+        ws = torch.empty(iofa.fa_softmax_workspace_bytes(3, 50000, xd.dtype), dtype=torch.uint8,
+                         device=dev)
+        iofa.fa_softmax_rows(xd, xd, None, ws)          # in place
+        torch.cuda.synchronize()
+        _check(x, xd, None, f"repair in place {dtype}")
+    finally:
+        iofa.fa_softmax_set_wait_limit(prev)
 
 
 def test_softmax_unaligned_rows_take_the_scalar_path(dev):
@@ -110,10 +157,12 @@ def test_softmax_stress_spread(dev):
         _check(x, y, lse, f"stress {dtype}")
 
 
-@pytest.mark.parametrize("rows,n,picked", [(32768, 8192, 48), (64, 1 << 22, 3)])
+@pytest.mark.parametrize("rows,n,picked", [(32768, 8192, 48), (4096, 1 << 16, 24),
+                                            (64, 1 << 22, 3)])
 def test_softmax_at_the_benchmarked_shapes(rows, n, picked, dev):
-    # the two shapes the bench times (rows of one chunk, and rows of 512
-    # chunks through the two-pass path), in the same launch configuration;
+    # the three shapes the bench times (rows of one chunk, rows of 4 slices
+    # through the one-pass form, rows of 512 chunks through the two passes),
+    # in the same launch configuration;
     # rows are independent, so sampled rows (and the first and last) are held
     # to the oracle's softmax of those rows
     x = _inputs(rows, n, "bf16", seed=rows + 1, spread=4.0)
