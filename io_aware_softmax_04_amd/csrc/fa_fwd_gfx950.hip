@@ -55,6 +55,11 @@ struct FusedCfg {
 // maximum bounds every exponential by 2^8, and the O accumulator is then
 // rescaled only on the (rare, wave-uniform) tiles that move m.
 constexpr float kRescaleSlack = 8.0f;
+// Query tiles an XCD runs at once: 32 CUs x 2 workgroups on MI355X.  Heads
+// with more query tiles alternate their key sweep's direction per round of
+// this many tiles (see the kernel), which measured 2.11x instead of 2.32x the
+// compulsory bytes at B1 H32 N16384 d128, in the same time.
+constexpr int kRoundTiles = 64;
 // Largest partial row sum (per lane, per tile) accepted without moving the
 // reference maximum.  It bounds every unnormalised weight, which is rounded
 // to the input type for the P V product: 2^32 for bf16 (range of fp32),
@@ -331,14 +336,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
+  // Sweep direction: an XCD runs kRoundTiles query tiles at once, so a head
+  // with more tiles streams its keys once per round of that many tiles.
+  // Odd rounds sweep the keys from the last tile to the first, starting on
+  // the tiles the previous round read last (still in the XCD's L2).  Only
+  // whole tiles (the masked ragged tile must come last) and whole sweeps.
+  const bool rev = !PARTIAL && !ragged && ((qt / kRoundTiles) & 1) != 0;
+  // first key of the t-th tile of the sweep; t >= NT gives a tile past the end
+  auto key0 = [&](int t) { return (rev && t < NT) ? (NT - 1 - t) * BC : t * BC; };
   TileCopy<D, BC, kSwzK> kcp;
   TileCopy<D, BC, kSwzV> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
   // a2 prologue: K_0 and K_1 in flight while Q is loaded
-  kcp.copy(Kh, 0, NK, kst[0]);
-  kcp.copy(Kh, BC, NK, kst[1]);
+  kcp.copy(Kh, key0(0), NK, kst[0]);
+  kcp.copy(Kh, key0(1), NK, kst[1]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
@@ -386,8 +399,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     // again before the wait and barrier (measured 0.8% faster at d = 128,
     // 3.8% at d = 64, bit-identical output)
     __builtin_amdgcn_s_setprio(1);
-    kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
-    vcp.copy(Vh, j * BC, NK, vst[P]);
+    kcp.copy(Kh, key0(j + 2), NK, kst[P]);
+    vcp.copy(Vh, key0(j), NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv_scores<1 - P, 1 - P>(p_prev, s_nxt);
     // d = 128 keeps its reads LEAD ahead for the whole tile, with three
@@ -411,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
                   vec8 (&p_cur)[C::KSTEPS]) {
     constexpr int P = decltype(par)::value;
-    vcp.copy(Vh, j * BC, NK, vst[P]);
+    vcp.copy(Vh, key0(j), NK, vst[P]);
     const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
                                : ws.template softmax<false>(s_cur, p_cur, c2, BC);
     if (j > 0) ws.template pv<1 - P>(p_prev);
@@ -425,8 +438,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
     last(P0{}, 0, sa, pb, pa);
   } else {
     // iteration 0: softmax_0 with scores_1
-    kcp.copy(Kh, 2 * BC, NK, kst[0]);
-    vcp.copy(Vh, 0, NK, vst[0]);
+    kcp.copy(Kh, key0(2), NK, kst[0]);
+    vcp.copy(Vh, key0(0), NK, vst[0]);
     {
       const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
       ws.template scores<1>(sb);

@@ -87,6 +87,23 @@ def test_fused_many_heads(dev):
     assert_parity(o, lse, o_ref, lse_ref, q.dtype, "many heads")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_long_heads_sweep_both_directions(d, dev):
+    # 96 query tiles per head: tiles 64-95 sweep the keys from the last tile
+    # to the first (heads with more tiles than an XCD runs at once alternate
+    # the direction per round); every element against the oracle
+    N = 12288
+    q, k, v = make_qkv(1, 2, N, d, "bf16", seed_base=4242 + d)
+    scale = default_scale(d)
+    _say(f"fused long heads d={d} N={N}")
+    o, lse = nan_outputs(q, dev)
+    iofa.fa_fwd(q.to(dev), k.to(dev), v.to(dev), o, lse, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    res = assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"long heads d={d}")
+    _say(f"  max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
+
+
 def test_fused_other_scales(dev):
     q, k, v = make_qkv(1, 2, 300, 128, "bf16", seed_base=91)
     for scale in (0.0, -0.125, 0.5):
