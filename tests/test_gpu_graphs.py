@@ -88,8 +88,10 @@ def test_fp8_forward_in_a_graph(dev):
                    [o, lse], dev)
 
 
-@pytest.mark.parametrize("n", [3000, 50000])
+@pytest.mark.parametrize("n", [3000, 50000, 20001, 1 << 20])
 def test_row_softmax_in_a_graph(n, dev):
+    # one chunk; 4 slices held in registers (one pass, with its clear and
+    # repair kernels); scalar two passes; 16-byte two passes (64 slices)
     g = torch.Generator().manual_seed(n)
     x = (torch.randn((4, n), generator=g) * 3).to(torch.bfloat16).to(dev)
     y = torch.empty_like(x)
