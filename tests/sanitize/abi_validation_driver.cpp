@@ -71,9 +71,24 @@ hipError_t __wrap__ZN4iofa12launch_naiveERKNS_9NaiveArgsE(const iofa::NaiveArgs&
   return hipErrorInvalidValue;
 }
 hipError_t __wrap__ZN4iofa14launch_softmaxERKNS_11SoftmaxArgsE(const iofa::SoftmaxArgs& a) {
-  check_launch(a.X && a.Y && a.rows >= 1 && a.n >= 1 && a.dtype >= 0 && a.dtype <= 2,
-               "launch_softmax");
+  bool ok = a.X && a.Y && a.rows >= 1 && a.n >= 1 && a.dtype >= 0 && a.dtype <= 2;
+  if (ok) {
+    // every grid the call may launch (at most one workgroup per pass-2 piece
+    // of every row) stays below 2^31 workgroups, and long rows have a workspace
+    const int64_t pieces = (a.n - 1) / iofa::softmax_piece(a.dtype) + 1;
+    ok = static_cast<__int128>(a.rows) * pieces < (static_cast<__int128>(1) << 31) &&
+         (a.n <= iofa::softmax_chunk(a.dtype) || a.workspace);
+  }
+  check_launch(ok, "launch_softmax");
   return hipErrorInvalidValue;
+}
+// Which form a softmax call takes asks the device for its capacity; here it
+// only checks what reaches it.
+int __wrap__ZN4iofa15softmax_x_readsERKNS_11SoftmaxArgsE(const iofa::SoftmaxArgs& a) {
+  ++g_launches;
+  if (!(a.rows >= 1 && a.n >= 1 && a.dtype >= 0 && a.dtype <= 2))
+    fail("softmax_x_reads received arguments fa_softmax_x_reads should have refused", "");
+  return 2;
 }
 hipError_t __wrap__ZN4iofa10launch_bwdERKNS_7BwdArgsE(const iofa::BwdArgs& a) {
   check_launch(a.Q && a.K && a.V && a.O && a.dO && a.LSE && a.dQ && a.dK && a.dV && a.stats &&
@@ -215,7 +230,13 @@ int main() {
                 empty, "fa_softmax_rows");
           after(fa_softmax_rows(p.q, p.o, nullptr, rows, n, dt, nullptr, 0, nullptr), empty,
                 "fa_softmax_rows (no workspace)");
+          const int reads = fa_softmax_x_reads(p.q, p.o, rows, n, dt);
+          const bool valid = dt >= 0 && dt <= 2 && rows >= 1 && n >= 1;
+          if (reads != (valid ? 2 : 0)) fail("fa_softmax_x_reads", "unexpected result");
         }
+  for (int polls : {0, 1, 400, -1, std::numeric_limits<int>::max(), std::numeric_limits<int>::min()})
+    (void)fa_softmax_set_wait_limit(polls);
+  if (fa_softmax_set_wait_limit(-1) != 400) fail("fa_softmax_set_wait_limit", "default not restored");
   std::printf("calls %ld, launches reached (intercepted) %ld, failures %d\n", g_calls, g_launches,
               g_fail);
   if (g_launches == 0) fail("driver", "no call reached a launcher");

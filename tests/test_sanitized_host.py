@@ -25,7 +25,8 @@ LAUNCHERS = ["_ZN4iofa12launch_fusedERKNS_7FwdArgsE",
              "_ZN4iofa14launch_softmaxERKNS_11SoftmaxArgsE",
              "_ZN4iofa10launch_bwdERKNS_7BwdArgsE",
              "_ZN4iofa10launch_fp8ERKNS_7Fp8ArgsE",
-             "_ZN4iofa15scratch_addressEPPv"]
+             "_ZN4iofa15scratch_addressEPPv",
+             "_ZN4iofa15softmax_x_readsERKNS_11SoftmaxArgsE"]
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
 
 
