@@ -101,12 +101,14 @@ def bytes_models(spec, br=128):
     }
 
 
-def fused_grid_items(spec, br=128, threads=256):
+def fused_grid_items(spec):
     """Work-items of the fused kernel's launch at the workload (its grid as
     the profiler reports it), which tells its dispatches apart from launches
     of the same kernel on other shapes in the same run (the split-KV
-    contrast's head share)."""
-    return spec["B"] * spec["H"] * math.ceil(spec["N"] / br) * threads
+    contrast's head share).  16-bit inputs: workgroups of 8 waves (256 query
+    rows) at d = 128, of 4 waves (128 rows) at d = 64."""
+    waves = 8 if spec["d"] == 128 else 4
+    return spec["B"] * spec["H"] * math.ceil(spec["N"] / (32 * waves)) * 64 * waves
 
 
 def _is_fused(row, spec, grid_key="Grid_Size"):

@@ -8,9 +8,10 @@
 // "核心思想" (blocks of the matrices staged in fast on-chip memory).
 //
 // gfx950 mapping (16-bit inputs):
-//   * workgroup = 4 waves = 128 query rows of one head, two workgroups per
-//     CU (8 waves, two per SIMD); each wave owns 32 query rows for the whole
-//     key sweep and keeps their Q fragments in VGPRs;
+//   * 8 waves per CU, two per SIMD: at d = 128 one workgroup of 8 waves =
+//     256 query rows of one head per CU, at d = 64 two workgroups of 4 waves
+//     = 128 rows each; each wave owns 32 query rows for the whole key sweep
+//     and keeps their Q fragments in VGPRs;
 //   * the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (fp32 acc): each
 //     lane then holds one query column, so the row max and row sum are
 //     in-lane over the tile's scores plus one exchange with the lane 32 apart
@@ -38,10 +39,24 @@
 
 namespace iofa {
 
+// Waves per workgroup of the 16-bit kernel.  At d = 128 all eight waves of a
+// CU form one workgroup, so its per-tile barrier keeps them on the same key
+// tile: with two 4-wave workgroups per CU one of them ran ahead of the other
+// (398 to 597 us for the same work at B1 H32 N16384), the workgroups of an
+// XCD drifted apart by up to 3.4 MiB of K and V, and heads whose keys exceed
+// the XCD's L2 were fetched 3.25 times instead of twice.  Eight waves
+// measured the same or faster at d = 128 (B2 H8 N8191 2% faster) and 4%
+// slower at d = 64 (B4 H16 N1024), which keeps four.
+template <int D>
+constexpr int kFusedWaves = D == 128 ? 8 : 4;
+
 template <int D, int BC>
 struct FusedCfg {
-  static constexpr int NW = 4;            // waves per workgroup
+  static constexpr int NW = kFusedWaves<D>;   // waves per workgroup
   static constexpr int BR = 32 * NW;      // query rows per workgroup
+  static constexpr int PER_CU = 8 / NW;   // workgroups per CU
+  // query tiles an XCD runs at once (32 CUs per XCD on MI355X)
+  static constexpr int ROUND = 32 * PER_CU;
   static constexpr int SB = BC / 32;      // 32-key score blocks per tile
   static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
   static constexpr int TILE = BC * D;     // elements of one K or V stage
@@ -55,11 +70,6 @@ struct FusedCfg {
 // maximum bounds every exponential by 2^8, and the O accumulator is then
 // rescaled only on the (rare, wave-uniform) tiles that move m.
 constexpr float kRescaleSlack = 8.0f;
-// Query tiles an XCD runs at once: 32 CUs x 2 workgroups on MI355X.  Heads
-// with more query tiles alternate their key sweep's direction per round of
-// this many tiles (see the kernel), which measured 2.11x instead of 2.32x the
-// compulsory bytes at B1 H32 N16384 d128, in the same time.
-constexpr int kRoundTiles = 64;
 // Largest partial row sum (per lane, per tile) accepted without moving the
 // reference maximum.  It bounds every unnormalised weight, which is rounded
 // to the input type for the P V product: 2^32 for bf16 (range of fp32),
@@ -309,7 +319,7 @@ struct WaveState {
 // combined by fa_merge_kernel.  Otherwise (one split) it writes O in the
 // input type and the final LSE.
 template <class T, int D, int BC, bool PARTIAL>
-__global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
+__global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ Out,
     float* __restrict__ Lse, int N, int BH, int num_qtiles, int num_splits, int num_wg,
@@ -336,16 +346,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16_kernel(
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
-  // Sweep direction: an XCD runs kRoundTiles query tiles at once, so a head
+  // Sweep direction: an XCD runs C::ROUND query tiles at once, so a head
   // with more tiles streams its keys once per round of that many tiles.
   // Odd rounds sweep the keys from the last tile to the first, starting on
-  // the tiles the previous round read last (still in the XCD's L2).  Only
-  // whole tiles (the masked ragged tile must come last) and whole sweeps.
-  const bool rev = !PARTIAL && !ragged && ((qt / kRoundTiles) & 1) != 0;
+  // the tiles the previous round read last.  Only whole tiles (the masked
+  // ragged tile must come last) and whole sweeps.
+  const bool rev = !PARTIAL && !ragged && ((qt / C::ROUND) & 1) != 0;
   // first key of the t-th tile of the sweep; t >= NT gives a tile past the end
   auto key0 = [&](int t) { return (rev && t < NT) ? (NT - 1 - t) * BC : t * BC; };
-  TileCopy<D, BC, kSwzK> kcp;
-  TileCopy<D, BC, kSwzV> vcp;
+  TileCopy<D, BC, kSwzK, C::NW> kcp;
+  TileCopy<D, BC, kSwzV, C::NW> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
@@ -601,8 +611,14 @@ int fused_key_tile(int dtype, int64_t d) {
   return d == 128 ? kFusedBC<128> : kFusedBC<64>;
 }
 
-int64_t fused_query_tile(int dtype) {
-  return dtype == kDtypeF32 ? 32 : FusedCfg<128, kFusedBC<128>>::BR;
+int64_t fused_query_tile(int dtype, int64_t d) {
+  if (dtype == kDtypeF32) return 32;
+  return d == 128 ? FusedCfg<128, kFusedBC<128>>::BR : FusedCfg<64, kFusedBC<64>>::BR;
+}
+
+int fused_waves_per_workgroup(int dtype, int64_t d) {
+  if (dtype == kDtypeF32) return 4;
+  return d == 128 ? FusedCfg<128, kFusedBC<128>>::NW : FusedCfg<64, kFusedBC<64>>::NW;
 }
 
 template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
@@ -611,7 +627,7 @@ static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) 
   const int qtiles = static_cast<int>((a.N + C::BR - 1) / C::BR);
   const int64_t wg = a.BH * splits * qtiles;
   hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC, PARTIAL>), dim3(static_cast<unsigned>(wg)),
-                     dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.Q),
+                     dim3(64 * C::NW), 0, a.stream, static_cast<const uint16_t*>(a.Q),
                      static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), out, lse,
                      static_cast<int>(a.N), static_cast<int>(a.BH), qtiles, splits,
                      static_cast<int>(wg), a.scale);
@@ -642,8 +658,8 @@ static hipError_t launch_any(const FwdArgs& a, int splits, void* out, float* lse
                     : launch32<64, PARTIAL>(a, splits, o, lse);
 }
 
-int64_t fused_workgroups(int dtype, int64_t BH, int64_t N, int64_t splits) {
-  const int64_t br = fused_query_tile(dtype);
+int64_t fused_workgroups(int dtype, int64_t d, int64_t BH, int64_t N, int64_t splits) {
+  const int64_t br = fused_query_tile(dtype, d);
   return BH * splits * ((N + br - 1) / br);
 }
 

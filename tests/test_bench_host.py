@@ -45,10 +45,12 @@ def test_byte_models_order():
 
 
 def test_fused_grid_of_the_benchmark_workload():
-    # B*H*ceil(N/128) workgroups of 256 work-items: 1024 workgroups at
-    # B2 H16 N4096, the grid the kernel trace lists for the fused forward
-    assert bench.fused_grid_items(WORKLOADS[3]) == 1024 * 256
-    assert bench.fused_grid_items(WORKLOADS[5]) == 2 * 8 * 64 * 256
+    # d = 128: B*H*ceil(N/256) workgroups of 512 work-items, 512 workgroups at
+    # B2 H16 N4096, the grid the kernel trace lists for the fused forward;
+    # d = 64: B*H*ceil(N/128) workgroups of 256
+    assert bench.fused_grid_items(WORKLOADS[3]) == 512 * 512
+    assert bench.fused_grid_items(WORKLOADS[5]) == 2 * 8 * 32 * 512
+    assert bench.fused_grid_items(WORKLOADS[2]) == 4 * 16 * 8 * 256
 
 
 def test_ceiling_output_split():
