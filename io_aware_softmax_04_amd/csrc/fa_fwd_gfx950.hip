@@ -44,7 +44,7 @@ namespace iofa {
 // tile: with two 4-wave workgroups per CU one of them ran ahead of the other
 // (398 to 597 us for the same work at B1 H32 N16384), the workgroups of an
 // XCD drifted apart by up to 3.4 MiB of K and V, and heads whose keys exceed
-// the XCD's L2 were fetched 3.25 times instead of twice.  Eight waves
+// the XCD's L2 were fetched 3.7 times instead of twice.  Eight waves
 // measured the same or faster at d = 128 (B2 H8 N8191 2% faster) and 4%
 // slower at d = 64 (B4 H16 N1024), which keeps four.
 template <int D>
@@ -54,9 +54,6 @@ template <int D, int BC>
 struct FusedCfg {
   static constexpr int NW = kFusedWaves<D>;   // waves per workgroup
   static constexpr int BR = 32 * NW;      // query rows per workgroup
-  static constexpr int PER_CU = 8 / NW;   // workgroups per CU
-  // query tiles an XCD runs at once (32 CUs per XCD on MI355X)
-  static constexpr int ROUND = 32 * PER_CU;
   static constexpr int SB = BC / 32;      // 32-key score blocks per tile
   static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
   static constexpr int TILE = BC * D;     // elements of one K or V stage
@@ -346,22 +343,14 @@ __global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fw
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
-  // Sweep direction: an XCD runs C::ROUND query tiles at once, so a head
-  // with more tiles streams its keys once per round of that many tiles.
-  // Odd rounds sweep the keys from the last tile to the first, starting on
-  // the tiles the previous round read last.  Only whole tiles (the masked
-  // ragged tile must come last) and whole sweeps.
-  const bool rev = !PARTIAL && !ragged && ((qt / C::ROUND) & 1) != 0;
-  // first key of the t-th tile of the sweep; t >= NT gives a tile past the end
-  auto key0 = [&](int t) { return (rev && t < NT) ? (NT - 1 - t) * BC : t * BC; };
   TileCopy<D, BC, kSwzK, C::NW> kcp;
   TileCopy<D, BC, kSwzV, C::NW> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
   // a2 prologue: K_0 and K_1 in flight while Q is loaded
-  kcp.copy(Kh, key0(0), NK, kst[0]);
-  kcp.copy(Kh, key0(1), NK, kst[1]);
+  kcp.copy(Kh, 0, NK, kst[0]);
+  kcp.copy(Kh, BC, NK, kst[1]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
@@ -409,8 +398,8 @@ __global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fw
     // again before the wait and barrier (measured 0.8% faster at d = 128,
     // 3.8% at d = 64, bit-identical output)
     __builtin_amdgcn_s_setprio(1);
-    kcp.copy(Kh, key0(j + 2), NK, kst[P]);
-    vcp.copy(Vh, key0(j), NK, vst[P]);
+    kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
+    vcp.copy(Vh, j * BC, NK, vst[P]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
     ws.template pv_scores<1 - P, 1 - P>(p_prev, s_nxt);
     // d = 128 keeps its reads LEAD ahead for the whole tile, with three
@@ -434,7 +423,7 @@ __global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fw
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
                   vec8 (&p_cur)[C::KSTEPS]) {
     constexpr int P = decltype(par)::value;
-    vcp.copy(Vh, key0(j), NK, vst[P]);
+    vcp.copy(Vh, j * BC, NK, vst[P]);
     const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
                                : ws.template softmax<false>(s_cur, p_cur, c2, BC);
     if (j > 0) ws.template pv<1 - P>(p_prev);
@@ -448,8 +437,8 @@ __global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fw
     last(P0{}, 0, sa, pb, pa);
   } else {
     // iteration 0: softmax_0 with scores_1
-    kcp.copy(Kh, key0(2), NK, kst[0]);
-    vcp.copy(Vh, key0(0), NK, vst[0]);
+    kcp.copy(Kh, 2 * BC, NK, kst[0]);
+    vcp.copy(Vh, 0, NK, vst[0]);
     {
       const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
       ws.template scores<1>(sb);

@@ -88,10 +88,11 @@ def test_fused_many_heads(dev):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_fused_long_heads_sweep_both_directions(d, dev):
-    # 96 query tiles per head: tiles 64-95 sweep the keys from the last tile
-    # to the first (heads with more tiles than an XCD runs at once alternate
-    # the direction per round); every element against the oracle
+def test_fused_long_heads_every_element(d, dev):
+    # heads with more query tiles than an XCD runs at once (48 workgroups of
+    # 256 rows at d = 128, 96 of 128 rows at d = 64, against 32 and 64 per
+    # XCD), so each head takes more than one round; every element against
+    # the oracle
     N = 12288
     q, k, v = make_qkv(1, 2, N, d, "bf16", seed_base=4242 + d)
     scale = default_scale(d)
