@@ -106,9 +106,11 @@ def fused_grid_items(spec):
     the profiler reports it), which tells its dispatches apart from launches
     of the same kernel on other shapes in the same run (the split-KV
     contrast's head share).  16-bit inputs: workgroups of 8 waves (256 query
-    rows) at d = 128, of 4 waves (128 rows) at d = 64."""
-    waves = 8 if spec["d"] == 128 else 4
-    return spec["B"] * spec["H"] * math.ceil(spec["N"] / (32 * waves)) * 64 * waves
+    rows) at d = 128 when there are at least as many of them as CUs (256),
+    else of 4 waves (128 rows)."""
+    heads = spec["B"] * spec["H"]
+    waves = 8 if spec["d"] == 128 and heads * math.ceil(spec["N"] / 256) >= 256 else 4
+    return heads * math.ceil(spec["N"] / (32 * waves)) * 64 * waves
 
 
 def _is_fused(row, spec, grid_key="Grid_Size"):

@@ -141,7 +141,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   const Region out[2] = {{O, tensor, "O"}, {LSE, lse, "LSE"}};
   st = check_aliasing(in, 3, out, 2);
   if (st != FA_OK) return st;
-  if (iofa::fused_workgroups(dtype, d, B * H, N, 1) >= (int64_t(1) << 31))
+  if (iofa::fused_workgroups(dtype, B * H, N, 1) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
   iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
   return hip_status(iofa::launch_fused(a), "fused forward launch");
@@ -184,8 +184,7 @@ int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
   int64_t g = requested;
   if (g <= 0) {
     // enough waves for one full round of the chip
-    const int64_t per_split =
-        iofa::fused_workgroups(dtype, d, B * H, N, 1) * iofa::fused_waves_per_workgroup(dtype, d);
+    const int64_t per_split = iofa::fused_waves(dtype, B * H, N, 1);
     g = (kTargetWaves + per_split - 1) / per_split;
     const int64_t longest = tiles / kMinTilesPerSplit;
     if (g > longest) g = longest;
@@ -227,7 +226,7 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
                          {workspace, g > 1 ? need : 0, "workspace"}};
   st = check_aliasing(in, 3, out, 3);
   if (st != FA_OK) return st;
-  if (iofa::fused_workgroups(dtype, d, B * H, N, g) >= (int64_t(1) << 31) ||
+  if (iofa::fused_workgroups(dtype, B * H, N, g) >= (int64_t(1) << 31) ||
       iofa::merge_workgroups(B * H * N, d) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
   iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};

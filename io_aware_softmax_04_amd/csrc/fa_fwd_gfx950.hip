@@ -8,10 +8,11 @@
 // "核心思想" (blocks of the matrices staged in fast on-chip memory).
 //
 // gfx950 mapping (16-bit inputs):
-//   * 8 waves per CU, two per SIMD: at d = 128 one workgroup of 8 waves =
-//     256 query rows of one head per CU, at d = 64 two workgroups of 4 waves
-//     = 128 rows each; each wave owns 32 query rows for the whole key sweep
-//     and keeps their Q fragments in VGPRs;
+//   * 8 waves per CU, two per SIMD: one workgroup of 8 waves = 256 query
+//     rows of one head per CU at d = 128 when the grid still gives every CU
+//     one, otherwise two workgroups of 4 waves = 128 rows each; each wave
+//     owns 32 query rows for the whole key sweep and keeps their Q fragments
+//     in VGPRs;
 //   * the wave computes S^T = K Q^T with v_mfma_f32_32x32x16 (fp32 acc): each
 //     lane then holds one query column, so the row max and row sum are
 //     in-lane over the tile's scores plus one exchange with the lane 32 apart
@@ -31,6 +32,7 @@
 //     each LDS read is a per-lane address computed once plus an immediate;
 //   * exponentials are exp2 with log2(e) folded into the fp32 scale; the row
 //     sum adds the fp32 exponentials, so the log-sum-exp keeps fp32 accuracy.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -39,20 +41,20 @@
 
 namespace iofa {
 
-// Waves per workgroup of the 16-bit kernel.  At d = 128 all eight waves of a
-// CU form one workgroup, so its per-tile barrier keeps them on the same key
-// tile: with two 4-wave workgroups per CU one of them ran ahead of the other
-// (398 to 597 us for the same work at B1 H32 N16384), the workgroups of an
-// XCD drifted apart by up to 3.4 MiB of K and V, and heads whose keys exceed
-// the XCD's L2 were fetched 3.7 times instead of twice.  Eight waves
-// measured the same or faster at d = 128 (B2 H8 N8191 2% faster) and 4%
-// slower at d = 64 (B4 H16 N1024), which keeps four.
-template <int D>
-constexpr int kFusedWaves = D == 128 ? 8 : 4;
-
-template <int D, int BC>
+// Waves per workgroup of the 16-bit kernel: 4 (two workgroups per CU) or 8
+// (one).  With 8, all eight waves of a CU share one per-tile barrier and so
+// stay on the same key tile: with two 4-wave workgroups per CU one of them
+// ran ahead of the other (398 to 597 us for the same work at B1 H32 N16384),
+// the workgroups of an XCD drifted apart by up to 3.4 MiB of K and V, and
+// heads whose keys exceed the XCD's L2 were fetched 3.7 times instead of
+// twice.  The launch takes 8 at d = 128 when that still gives every CU a
+// workgroup (measured the same or faster there, B2 H8 N8191 2% faster), and
+// 4 otherwise (at d = 64 8 measured 4% slower at B4 H16 N1024; a grid of
+// fewer 8-wave workgroups than CUs would leave CUs idle).  Both forms do
+// the same arithmetic per wave, so their results are identical.
+template <int D, int BC, int NW_ = 4>
 struct FusedCfg {
-  static constexpr int NW = kFusedWaves<D>;   // waves per workgroup
+  static constexpr int NW = NW_;          // waves per workgroup
   static constexpr int BR = 32 * NW;      // query rows per workgroup
   static constexpr int SB = BC / 32;      // 32-key score blocks per tile
   static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
@@ -315,13 +317,13 @@ struct WaveState {
 // q, :] and its log-sum-exp to Lse[(split*BH + bh), q]; the partials are
 // combined by fa_merge_kernel.  Otherwise (one split) it writes O in the
 // input type and the final LSE.
-template <class T, int D, int BC, bool PARTIAL>
-__global__ __launch_bounds__(64 * kFusedWaves<D>, 8 / kFusedWaves<D>) void fa_fwd_16_kernel(
+template <class T, int D, int BC, bool PARTIAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ Out,
     float* __restrict__ Lse, int N, int BH, int num_qtiles, int num_splits, int num_wg,
     float scale) {
-  using C = FusedCfg<D, BC>;
+  using C = FusedCfg<D, BC, NW>;
   using vec8 = typename T::vec8;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::SMEM];
   const uint32_t sm = lds_address(smem);
@@ -600,27 +602,51 @@ int fused_key_tile(int dtype, int64_t d) {
   return d == 128 ? kFusedBC<128> : kFusedBC<64>;
 }
 
-int64_t fused_query_tile(int dtype, int64_t d) {
-  if (dtype == kDtypeF32) return 32;
-  return d == 128 ? FusedCfg<128, kFusedBC<128>>::BR : FusedCfg<64, kFusedBC<64>>::BR;
+// Query rows per workgroup of the form with the most workgroups (the grid
+// limit check) and waves of a launch (the split-KV heuristic).
+int64_t fused_query_tile(int dtype) { return dtype == kDtypeF32 ? 32 : FusedCfg<128, 32>::BR; }
+
+int64_t fused_waves(int dtype, int64_t BH, int64_t N, int64_t splits) {
+  const int64_t br = fused_query_tile(dtype);
+  return BH * splits * ((N + br - 1) / br) * 4;
 }
 
-int fused_waves_per_workgroup(int dtype, int64_t d) {
-  if (dtype == kDtypeF32) return 4;
-  return d == 128 ? FusedCfg<128, kFusedBC<128>>::NW : FusedCfg<64, kFusedBC<64>>::NW;
+// CUs of the current device (256 if it cannot be found out).
+static int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
-template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
-static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) {
-  using C = FusedCfg<D, BC>;
+template <class T, int D, bool PARTIAL, int BC, int NW>
+static hipError_t launch16_nw(const FwdArgs& a, int splits, void* out, float* lse) {
+  using C = FusedCfg<D, BC, NW>;
   const int qtiles = static_cast<int>((a.N + C::BR - 1) / C::BR);
   const int64_t wg = a.BH * splits * qtiles;
-  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC, PARTIAL>), dim3(static_cast<unsigned>(wg)),
-                     dim3(64 * C::NW), 0, a.stream, static_cast<const uint16_t*>(a.Q),
+  hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC, PARTIAL, NW>), dim3(static_cast<unsigned>(wg)),
+                     dim3(64 * NW), 0, a.stream, static_cast<const uint16_t*>(a.Q),
                      static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), out, lse,
                      static_cast<int>(a.N), static_cast<int>(a.BH), qtiles, splits,
                      static_cast<int>(wg), a.scale);
   return hipGetLastError();
+}
+
+template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
+static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) {
+  if constexpr (D == 128) {
+    constexpr int64_t BR8 = FusedCfg<D, BC, 8>::BR;
+    if (a.BH * splits * ((a.N + BR8 - 1) / BR8) >= device_cus())
+      return launch16_nw<T, D, PARTIAL, BC, 8>(a, splits, out, lse);
+  }
+  return launch16_nw<T, D, PARTIAL, BC, 4>(a, splits, out, lse);
 }
 
 template <int D, bool PARTIAL>
@@ -647,8 +673,8 @@ static hipError_t launch_any(const FwdArgs& a, int splits, void* out, float* lse
                     : launch32<64, PARTIAL>(a, splits, o, lse);
 }
 
-int64_t fused_workgroups(int dtype, int64_t d, int64_t BH, int64_t N, int64_t splits) {
-  const int64_t br = fused_query_tile(dtype, d);
+int64_t fused_workgroups(int dtype, int64_t BH, int64_t N, int64_t splits) {
+  const int64_t br = fused_query_tile(dtype);
   return BH * splits * ((N + br - 1) / br);
 }
 

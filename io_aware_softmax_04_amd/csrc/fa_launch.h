@@ -116,13 +116,14 @@ struct Fp8Args {
 int64_t fp8_workgroups(int64_t BH, int64_t N);
 hipError_t launch_fp8(const Fp8Args& a);
 
-// Keys per tile, query rows per workgroup and waves per workgroup of the
-// fused kernels.
+// Keys per tile of the fused kernels, and query rows per workgroup of their
+// form with the most workgroups.
 int fused_key_tile(int dtype, int64_t d);
-int64_t fused_query_tile(int dtype, int64_t d);
-int fused_waves_per_workgroup(int dtype, int64_t d);
-// Workgroups the fused launch uses (for the grid-size limit check).
-int64_t fused_workgroups(int dtype, int64_t d, int64_t BH, int64_t N, int64_t splits);
+int64_t fused_query_tile(int dtype);
+// At most this many workgroups per fused launch (the grid-size limit check).
+int64_t fused_workgroups(int dtype, int64_t BH, int64_t N, int64_t splits);
+// Waves of a fused launch (the split-KV heuristic).
+int64_t fused_waves(int dtype, int64_t BH, int64_t N, int64_t splits);
 int64_t merge_workgroups(int64_t rows, int64_t d);
 // Largest grid among the naive path's three launches.
 int64_t naive_max_workgroups(int dtype, int64_t BH, int64_t N);
