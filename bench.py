@@ -16,6 +16,7 @@ import argparse
 import hashlib
 import json
 import math
+import re
 import os
 import sys
 import time
@@ -113,8 +114,13 @@ def fused_grid_items(spec):
     return heads * math.ceil(spec["N"] / (32 * waves)) * 64 * waves
 
 
+# fa_fwd_16_kernel<T, D, BC, PARTIAL, waves>: the fused forward proper has
+# PARTIAL = false (the split-KV partial pass is true)
+_FUSED_FULL = re.compile(FUSED_KERNEL_NAME + r"<[^<>]*?, \d+, \d+, false(?:, \d+)?>")
+
+
 def _is_fused(row, spec, grid_key="Grid_Size"):
-    return (FUSED_KERNEL_NAME in row["Kernel_Name"] and ", false>" in row["Kernel_Name"]
+    return (_FUSED_FULL.search(row["Kernel_Name"]) is not None
             and int(row[grid_key]) == fused_grid_items(spec))
 
 

@@ -79,14 +79,30 @@ def _fake_trace(directory, fused_ns, other_ns):
     rows = ["Kernel_Name,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp"]
     t = 1000
     for ns in fused_ns:
-        rows.append(f'"void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false>(...)",{grid},1,1,{t},{t + ns}')
+        rows.append(f'"void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false, 8>(...)",'
+                    f'{grid},1,1,{t},{t + ns}')
         t += ns + 10
+    # the split-KV partial pass of the same kernel at the same grid is not the fused forward
+    rows.append(f'"void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, true, 8>(...)",{grid},1,1,{t},{t + 999_999}')
+    t += 999_999 + 10
     for ns in other_ns:
         rows.append(f'"void iofa::naive_pv_16<iofa::Bf16, 128>(...)",1024,1,1,{t},{t + ns}')
         t += ns + 10
     os.makedirs(directory, exist_ok=True)
     with open(os.path.join(directory, "run_kernel_trace.csv"), "w") as fh:
         fh.write("\n".join(rows) + "\n")
+
+
+def test_fused_rows_are_told_apart_by_name_and_grid():
+    spec = WORKLOADS[3]
+    grid = bench.fused_grid_items(spec)
+    for name, want in (("void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false, 8>(...)", True),
+                       ("void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, false>(...)", True),
+                       ("void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, true, 8>(...)", False),
+                       ("void iofa::fa_fwd_fp8_kernel<128>(...)", False)):
+        assert bench._is_fused({"Kernel_Name": name, "Grid_Size": grid}, spec) is want, name
+    assert not bench._is_fused({"Kernel_Name": "void iofa::fa_fwd_16_kernel<iofa::Bf16, 128, 32, "
+                                               "false, 4>(...)", "Grid_Size": grid // 8}, spec)
 
 
 def test_trace_summary_quotes_the_profiled_run(tmp_path):
