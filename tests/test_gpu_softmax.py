@@ -135,6 +135,36 @@ def test_softmax_repair_path_matches_oracle(dtype, dev):
         iofa.fa_softmax_set_wait_limit(prev)
 
 
+def test_softmax_resident_beside_a_busy_stream(dev):
+    # the one-pass form needs every slice of a row resident at once; with the
+    # fused forward occupying the chip from another stream that may not hold,
+    # and slices whose wait runs out go to the repair kernel: the result must
+    # not change
+    from workloads import default_scale, make_qkv
+    q, k, v = (t.to(dev) for t in make_qkv(2, 16, 4096, 128, "bf16", seed_base=808))
+    o = torch.empty_like(q)
+    lse_f = torch.empty((2, 16, 4096), dtype=torch.float32, device=dev)
+    busy, side = torch.cuda.Stream(), torch.cuda.Stream()
+    cases = [_inputs(48, 1 << 19, "bf16", seed=91), _inputs(64, 100000, "fp32", seed=92)]
+    for i, x in enumerate(cases):
+        xd = x.to(dev)
+        y = torch.empty_like(xd)
+        lse = torch.empty(xd.shape[0], dtype=torch.float32, device=dev)
+        ws = torch.empty(iofa.fa_softmax_workspace_bytes(*xd.shape, xd.dtype), dtype=torch.uint8,
+                         device=dev)
+        assert iofa.fa_softmax_x_reads(xd, y) == 1
+        torch.cuda.synchronize()
+        with torch.cuda.stream(busy):
+            for _ in range(20):
+                iofa.fa_fwd(q, k, v, o, lse_f, default_scale(128))
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                iofa.fa_softmax_rows(xd, y, lse, ws)
+        torch.cuda.synchronize()
+        print(f"softmax beside a busy stream, case {i}: {tuple(xd.shape)} {xd.dtype}", flush=True)
+        _check(x, y, lse, f"beside a busy stream {i}")
+
+
 def test_softmax_unaligned_rows_take_the_scalar_path(dev):
     # a base one element past a 16-byte boundary and an odd row length
     buf = _inputs(1, 5 * 9001 + 1, "bf16", seed=5).view(-1).to(dev)
