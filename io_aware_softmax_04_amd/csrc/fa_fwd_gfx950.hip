@@ -22,13 +22,16 @@
 //     V tile through the transposing ds_read_b64_tr_b16;
 //   * K and V tiles (32 keys at d = 128, 64 at d = 64) are copied global ->
 //     LDS directly (buffer_load_dwordx4 ... lds, swizzled rows, range-checked
-//     so rows past N arrive as zeros) into two stages each;
+//     so rows past N arrive as zeros) into rings of four stages each: a K
+//     tile three iterations ahead, a V tile one ahead;
 //   * three-stage software pipeline: while the VALU computes the softmax of
 //     tile j, the MFMA unit runs P_{j-1} V_{j-1} and the scores of tile j+1,
-//     none of which depend on that softmax; one barrier per tile; the score
+//     none of which depend on that softmax; one barrier per two tiles (the
+//     four-stage rings keep a barrier between every copy and its reads, and
+//     between every read and the copy that overwrites the stage); the score
 //     and P V products alternate, and the wave runs them at raised issue
 //     priority, dropped for the wait and barrier that close the tile;
-//   * the loop is unrolled by two so every LDS stage offset is a constant:
+//   * the loop is unrolled by four so every LDS stage offset is a constant:
 //     each LDS read is a per-lane address computed once plus an immediate;
 //   * exponentials are exp2 with log2(e) folded into the fp32 scale; the row
 //     sum adds the fp32 exponentials, so the log-sum-exp keeps fp32 accuracy.
@@ -60,7 +63,8 @@ struct FusedCfg {
   static constexpr int KSTEPS = BC / 16;  // 16-key steps of P V per tile
   static constexpr int TILE = BC * D;     // elements of one K or V stage
   static constexpr uint32_t TB = TILE * 2u;   // bytes of one stage
-  static constexpr int SMEM = 4 * TILE;   // K stages 0, 1, then V stages 0, 1
+  static constexpr int STAGES = 4;        // ring of LDS stages for K and for V
+  static constexpr int SMEM = 2 * STAGES * TILE;   // K stages 0..3, then V stages 0..3
 };
 
 // The running maximum is only moved when a tile's maximum exceeds it by more
@@ -115,7 +119,7 @@ struct WaveState {
     for (int cb = 0; cb < D / 32; ++cb) {
       const int col = 32 * cb + 16 * (g & 1) + 4 * (t & 3);
       const int chunk = (col >> 3) ^ v_swz<D>(row);
-      v_addr[cb] = smem_byte + 2 * C::TB + static_cast<uint32_t>(row * D + chunk * 8 + (col & 7)) * 2u;
+      v_addr[cb] = smem_byte + C::STAGES * C::TB + static_cast<uint32_t>(row * D + chunk * 8 + (col & 7)) * 2u;
     }
   }
 
@@ -303,14 +307,19 @@ struct WaveState {
 
 // Per wave, tile t of the key sweep (NT tiles) is processed in three steps:
 // its scores in iteration t-1, its softmax in iteration t, its P V product
-// in iteration t+1.  K tile t lives in K stage t%2, copied in iteration t-2;
-// V tile t in V stage t%2, copied in iteration t.  Iteration j (P = j%2):
-//   top     direct copies K_{j+2} -> K stage P (last read in iteration j-1)
-//           and V_j -> V stage P (last read in iteration j-1);
-//   middle  softmax_j (VALU) interleaved with P_{j-1} V_{j-1} (V stage 1-P)
-//           and scores_{j+1} (K stage 1-P) on the MFMA unit;
-//   bottom  rescale of O if the reference maximum moved; wait for this
-//           iteration's copies; barrier.
+// in iteration t+1.  K tile t lives in K stage t%4, copied in iteration t-3;
+// V tile t in V stage t%4, copied in iteration t-1.  Iteration j (P = j%4):
+//   top     direct copies K_{j+3} -> K stage (j+3)%4 (last read in iteration
+//           j-2) and V_{j+1} -> V stage (j+1)%4 (last read in iteration j-2);
+//   middle  softmax_j (VALU) interleaved with P_{j-1} V_{j-1} (V stage
+//           (j-1)%4) and scores_{j+1} (K stage (j+1)%4) on the MFMA unit;
+//   bottom  rescale of O if the reference maximum moved; after odd j only:
+//           wait for the copies in flight, barrier.
+// Barriers after every odd iteration (and after iteration 0) put one between
+// each copy and its first read (a K copy in j and its read in j+2, a V copy
+// in j and its read in j+2) and between each last read and the overwriting
+// copy (read in j-2, copy in j); one barrier per tile measured 2.2-2.7%
+// slower at B2 H16 N4096, B2 H8 N8191 and B1 H32 N16384, bit-identical.
 //
 // With PARTIAL the workgroup covers only the keys of its split (key_range)
 // and writes the normalised partial output in fp32 to Out[(split*BH + bh),
@@ -327,8 +336,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   using vec8 = typename T::vec8;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[C::SMEM];
   const uint32_t sm = lds_address(smem);
-  const uint32_t kst[2] = {sm, sm + C::TB};
-  const uint32_t vst[2] = {sm + 2 * C::TB, sm + 3 * C::TB};
+  const uint32_t kst[4] = {sm, sm + C::TB, sm + 2 * C::TB, sm + 3 * C::TB};
+  const uint32_t vst[4] = {sm + 4 * C::TB, sm + 5 * C::TB, sm + 6 * C::TB, sm + 7 * C::TB};
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -350,9 +359,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
-  // a2 prologue: K_0 and K_1 in flight while Q is loaded
+  // a2 prologue: K_0, K_1, K_2 and V_0 in flight while Q is loaded
   kcp.copy(Kh, 0, NK, kst[0]);
   kcp.copy(Kh, BC, NK, kst[1]);
+  kcp.copy(Kh, 2 * BC, NK, kst[2]);
+  vcp.copy(Vh, 0, NK, vst[0]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
@@ -379,7 +390,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   f32x16 sa[C::SB], sb[C::SB];
   vec8 pa[C::KSTEPS], pb[C::KSTEPS];
   ws.template scores<0>(sa);
-  __syncthreads();   // K stage 0 is refilled in iteration 0
 
   constexpr int NM = 2 * (D / 16) * C::SB;          // products per iteration
   constexpr int NRD = (D / 16) * C::SB + 2 * NM / 2;  // K reads + 2 per P V product
@@ -395,15 +405,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   // one full iteration j with parity P (compile-time)
   auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
                        vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
-    constexpr int P = decltype(par)::value;
+    constexpr int P = decltype(par)::value;   // j % 4
     // raised issue priority from the copies through the products; dropped
     // again before the wait and barrier (measured 0.8% faster at d = 128,
     // 3.8% at d = 64, bit-identical output)
     __builtin_amdgcn_s_setprio(1);
-    kcp.copy(Kh, (j + 2) * BC, NK, kst[P]);
-    vcp.copy(Vh, j * BC, NK, vst[P]);
+    kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
+    vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
     const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
-    ws.template pv_scores<1 - P, 1 - P>(p_prev, s_nxt);
+    ws.template pv_scores<(P + 3) % 4, (P + 1) % 4>(p_prev, s_nxt);
     // d = 128 keeps its reads LEAD ahead for the whole tile, with three
     // vector instructions per product (four: 1.1-1.5% slower at B2 H16
     // N4096, B2 H8 N8191 and B1 H32 N16384; two: 0.5% slower); at d = 64 the
@@ -418,29 +428,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
     float alpha;
     if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
     __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (P % 2 == 1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   };
   // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
   auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
                   vec8 (&p_cur)[C::KSTEPS]) {
-    constexpr int P = decltype(par)::value;
-    vcp.copy(Vh, j * BC, NK, vst[P]);
+    constexpr int P = decltype(par)::value;   // j % 4
     const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
                                : ws.template softmax<false>(s_cur, p_cur, c2, BC);
-    if (j > 0) ws.template pv<1 - P>(p_prev);
+    if (j > 0) ws.template pv<(P + 3) % 4>(p_prev);
     bottom(alpha);
     ws.template pv<P>(p_cur);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
 
   if (NT == 1) {
     last(P0{}, 0, sa, pb, pa);
   } else {
     // iteration 0: softmax_0 with scores_1
-    kcp.copy(Kh, 2 * BC, NK, kst[0]);
-    vcp.copy(Vh, 0, NK, vst[0]);
+    kcp.copy(Kh, 3 * BC, NK, kst[3]);
+    vcp.copy(Vh, BC, NK, vst[1]);
     {
       const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
       ws.template scores<1>(sb);
@@ -448,15 +461,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
       interleave_mfma_valu<NS1, NS1, 2, 4>();
       bottom(alpha);
     }
-    // iterations 1 .. NT-2, two per trip so register sets and stages alternate
+    // iterations 1 .. NT-2, four per trip so register sets alternate and
+    // every stage index is a constant
     int j = 1;
-    for (; j + 1 < NT - 1; j += 2) {
+    for (; j + 3 < NT - 1; j += 4) {
       iteration(P1{}, j, sb, sa, pa, pb);
-      iteration(P0{}, j + 1, sa, sb, pb, pa);
+      iteration(P2{}, j + 1, sa, sb, pb, pa);
+      iteration(P3{}, j + 2, sb, sa, pa, pb);
+      iteration(P0{}, j + 3, sa, sb, pb, pa);
     }
     if (j < NT - 1) {
       iteration(P1{}, j, sb, sa, pa, pb);
-      last(P0{}, j + 1, sa, pb, pa);
+      if (j + 1 < NT - 1) {
+        iteration(P2{}, j + 1, sa, sb, pb, pa);
+        if (j + 2 < NT - 1) {
+          iteration(P3{}, j + 2, sb, sa, pa, pb);
+          last(P0{}, j + 3, sa, pb, pa);
+        } else {
+          last(P3{}, j + 2, sb, pa, pb);
+        }
+      } else {
+        last(P2{}, j + 1, sa, pb, pa);
+      }
     } else {
       last(P1{}, j, sb, pa, pb);
     }
