@@ -323,14 +323,19 @@ BENCH_STDOUT = "bench_stdout.txt"
 # the traffic passes run the fused and the naive paths only, a few launches each
 TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-softmax --no-backward --no-fp8 "
                       "--no-ceiling --no-cpu-baseline")
-# Shader counters, in two rocprofv3 --pmc passes of at most 8 SQ counters each
+# Shader counters, in rocprofv3 --pmc passes of at most 8 SQ counters each
+# (a and b for every kernel; c, the LDS pass, optional)
 SQ_PASSES = {
     "a": ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
           "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES", "SQ_WAVE_CYCLES"],
     "b": ["SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS",
           "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
           "SQ_INSTS_SALU"],
+    "c": ["SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_IDX_ACTIVE",
+          "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_CMD_FIFO_FULL",
+          "SQ_LDS_DATA_FIFO_FULL"],
 }
+COMPUTE_UNITS = 256
 SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
 SIMDS = 1024                 # 256 CUs x 4
 # Kernels the counter summary covers: (name filter, FLOPs per MFMA instruction,
@@ -367,7 +372,11 @@ def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
     which a vector instruction issued while they were busy.  SQ_WAVE_CYCLES,
     SQ_WAIT_ANY and SQ_WAIT_INST_LDS are wave-cycles in units of 4 cycles:
     their ratios are the fraction of a wave's lifetime spent waiting, and
-    waiting to issue an LDS instruction."""
+    waiting to issue an LDS instruction.  From the optional third pass:
+    SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte units read from LDS, and
+    SQ_LDS_IDX_ACTIVE the cycles the CUs' LDS spent on indexed accesses
+    (summed over CUs), so their ratio is the bytes the LDS returned per
+    active cycle and the latter over CUs x kernel cycles its busy fraction."""
     import csv
     import glob
     per = {}
@@ -406,7 +415,7 @@ def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
         "",
         "```",
     ]
-    for name, d in zip(("a", "b"), pmc_dirs):
+    for name, d in zip(("a", "b", "c"), pmc_dirs):
         lines.append(f"rocprofv3 --pmc {' '.join(SQ_PASSES[name])} --kernel-include-regex "
                      f"'{regex}' -d {d} -o run --output-format csv "
                      f"-- python bench.py --workload {index} {bench_args}")
@@ -449,6 +458,21 @@ def summarise_sq(pmc_dirs, index, spec, which="fused", out_dir=None):
                      f"{(avg['SQ_INSTS_VALU'] - mfma + avg['SQ_INSTS_LDS']) / mfma:.2f} |")
         if "SQ_INSTS_SALU" in avg:
             lines.append(f"| scalar instructions per wave | {avg['SQ_INSTS_SALU'] / waves:.0f} |")
+    if "SQ_LDS_IDX_ACTIVE" in avg:
+        lds_bytes = 64.0 * avg["SQ_INSTS_LDS_LOAD_BANDWIDTH"]
+        active = avg["SQ_LDS_IDX_ACTIVE"]
+        lines += [f"| LDS bytes read per dispatch (64 x SQ_INSTS_LDS_LOAD_BANDWIDTH) | "
+                  f"{lds_bytes:.4g} |",
+                  f"| LDS bytes per active cycle (bytes / SQ_LDS_IDX_ACTIVE) | "
+                  f"{lds_bytes / active:.0f} |",
+                  f"| LDS busy (SQ_LDS_IDX_ACTIVE / CUs / cycles) | "
+                  f"{active / (COMPUTE_UNITS * cycles):.3f} |",
+                  f"| LDS bank / address conflict cycles per active cycle | "
+                  f"{avg['SQ_LDS_BANK_CONFLICT'] / active:.3f} / "
+                  f"{avg['SQ_LDS_ADDR_CONFLICT'] / active:.3f} |",
+                  f"| LDS command / data FIFO full cycles per active cycle | "
+                  f"{avg['SQ_LDS_CMD_FIFO_FULL'] / active:.4f} / "
+                  f"{avg['SQ_LDS_DATA_FIFO_FULL'] / active:.4f} |"]
     lines += ["", f"kernel_sources_sha256_16: {sources_hash()}", ""]
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"),
                         f"sq_counters_{tag}_{workload_tag(spec)}.md")

@@ -200,6 +200,37 @@ def test_shader_counter_summary_with_unequal_passes(tmp_path):
     assert "| 10 / 100 / 1 / 5 |" in text
 
 
+def test_shader_counter_summary_with_the_lds_pass(tmp_path):
+    # 300000 cycles; the LDS returns 2^33 bytes in 2^25 active cycles summed
+    # over the CUs: 256 bytes per active cycle, busy 2^25 / (256 x 300000)
+    cyc = 300000.0
+    a = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * bench.SIMDS * cyc,
+         "SQ_INSTS_VALU": 100.0, "SQ_INSTS_MFMA": 10.0, "SQ_INSTS_LDS": 5.0,
+         "SQ_INSTS_VALU_TRANS_F32": 1.0, "SQ_WAVES": 1.0, "SQ_WAVE_CYCLES": 1.0e8}
+    b = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_WAVE_CYCLES": 1.0e8, "SQ_WAIT_ANY": 3.0e7,
+         "SQ_WAIT_INST_LDS": 1.0e7, "SQ_VALU_MFMA_COEXEC_CYCLES": 0.1 * bench.SIMDS * cyc,
+         "SQ_ACTIVE_INST_VALU": 0.1 * bench.SIMDS * cyc,
+         "SQ_ACTIVE_INST_LDS": 0.1 * bench.SIMDS * cyc, "SQ_INSTS_SALU": 7.0}
+    c = {"SQ_BUSY_CYCLES": 32 * cyc, "SQ_INSTS_LDS": 5.0, "SQ_INSTS_LDS_LOAD_BANDWIDTH": 2.0 ** 27,
+         "SQ_LDS_IDX_ACTIVE": 2.0 ** 25, "SQ_LDS_BANK_CONFLICT": 2.0 ** 23,
+         "SQ_LDS_ADDR_CONFLICT": 0.0, "SQ_LDS_CMD_FIFO_FULL": 2.0 ** 15,
+         "SQ_LDS_DATA_FIFO_FULL": 0.0}
+    assert sorted(c) == sorted(bench.SQ_PASSES["c"])
+    name = "void iofa::bwd_dq_kernel<iofa::Bf16, 128>(...)"
+    for k, v in (("a", a), ("b", b), ("c", c)):
+        _pmc_csv(str(tmp_path / k), name, 1024, v, 200000)
+    out = tmp_path / "out"
+    out.mkdir()
+    text = open(bench.summarise_sq([str(tmp_path / k) for k in "abc"], 3, WORKLOADS[3],
+                                   "bwd_dq", out_dir=str(out))).read()
+    assert "rocprofv3 --pmc " + " ".join(bench.SQ_PASSES["c"]) in text
+    assert "(64 x SQ_INSTS_LDS_LOAD_BANDWIDTH) | 8.59e+09 |" in text
+    assert "(bytes / SQ_LDS_IDX_ACTIVE) | 256 |" in text
+    assert f"(SQ_LDS_IDX_ACTIVE / CUs / cycles) | {2 ** 25 / (256 * cyc):.3f} |" in text
+    assert "conflict cycles per active cycle | 0.250 / 0.000 |" in text
+    assert "FIFO full cycles per active cycle | 0.0010 / 0.0000 |" in text
+
+
 def test_traffic_calibration_sums_a_split_copy(tmp_path):
     # the 1024 MiB calibration copy ran as two dispatches of 512 MiB: the
     # scale comes from their sum, not their mean
