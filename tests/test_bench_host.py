@@ -274,3 +274,20 @@ def test_traffic_calibration_sums_a_split_copy(tmp_path):
     assert "scaled by 4.0000 (fetch) and 2.0000 (write)" not in text
     assert "scaled by 2.0000 (fetch) and 1.0000 (write)" in text
     assert f"bytes_per_launch: {round(49260.0 * 1024 * 2 + 33280.0 * 1024)}" in text
+
+
+def test_cpu_baseline_repeats_a_whole_workload_that_finishes_early():
+    # a one-head workload the oracle finishes in milliseconds: the whole of
+    # it is the sample, repeated (at most 8 times) toward the target seconds
+    import torch
+    from workloads import make_qkv
+    spec = {"B": 1, "H": 1, "N": 64, "d": 64, "dtype": "bf16"}
+    q, k, v = make_qkv(1, 1, 64, 64, "bf16", seed_base=7)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32)
+    r = bench.cpu_baseline(q, k, v, 0.125, spec, o, lse, target_s=5.0)
+    assert r["repetitions"] == 8
+    assert "query rows 0..63 of 64 (100.0% of the workload's FLOPs), computed 8 times" in r["sample"]
+    assert r["value"] > 0 and r["seconds"] > 0
+    # the parity figures compare the given output (zeros here) with the oracle's
+    assert r["sample_parity"]["max_abs"] > 0
