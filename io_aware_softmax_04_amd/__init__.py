@@ -1,20 +1,19 @@
 """Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
 
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_fwd_splitkv_noalloc``,
-``fa_splitkv_num_splits``,
-``fa_splitkv_workspace_bytes``, ``fa_merge_partials``, ``fa_softmax_rows``,
-``fa_softmax_workspace_bytes``, ``fa_softmax_x_reads``, ``fa_softmax_set_wait_limit``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_fp8``,
-``fa_naive_fwd``,
-``fa_naive_workspace_bytes``, ``fa_status_string``, ``fa_last_error`` and
-``fa_version`` carry the names
-and meaning of the entry points declared in ``include/fa_api.h``; they only
+``fa_splitkv_num_splits``, ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``,
+``fa_softmax_rows``, ``fa_softmax_workspace_bytes``, ``fa_softmax_x_reads``,
+``fa_softmax_set_wait_limit``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
+``fa_fwd_fp8``, ``fa_naive_fwd``, ``fa_naive_workspace_bytes``,
+``fa_status_string``, ``fa_last_error`` and ``fa_version`` carry the names and
+meaning of the entry points declared in ``include/fa_api.h``; they only
 marshal torch tensors into pointers, sizes and the current HIP stream.  Every
 step of the computation runs in the HIP kernels of ``libiofa.so``; there is
 no CPU fallback, and a missing library raises instead of computing.
 
-``forward``, ``forward_splitkv``, ``forward_fp8`` and ``naive_forward`` are conveniences
-that allocate the outputs (and workspaces) with torch and call the entry
-points.
+``forward``, ``forward_splitkv``, ``forward_fp8``, ``backward``, ``softmax`` and
+``naive_forward`` are conveniences that allocate the outputs (and workspaces)
+with torch and call the entry points.
 """
 
 import ctypes
