@@ -87,6 +87,43 @@ def test_fused_many_heads(dev):
     assert_parity(o, lse, o_ref, lse_ref, q.dtype, "many heads")
 
 
+# Lengths for the 8-wave form: one to nine 32-key tiles, ragged tails, and
+# the first length that takes two query tiles of 256 rows per head.
+EIGHT_WAVE_N = [1, 17, 32, 33, 64, 65, 100, 129, 255, 256, 257]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fused_8wave_form_short_and_ragged(dtype, dev):
+    # At d = 128 the launch takes workgroups of 8 waves (256 query rows) when
+    # B*H*ceil(N/256) reaches the CU count (256 on MI355X); 256 heads do so at
+    # every length here.  Every element of O and LSE, NaN-filled before the
+    # launch, against the oracle.
+    H = 256
+    for N in EIGHT_WAVE_N:
+        q, k, v = make_qkv(1, H, N, 128, dtype, seed_base=9000 + N)
+        scale = default_scale(128)
+        _say(f"fused 8-wave {dtype} H={H} N={N}")
+        o, lse = nan_outputs(q, dev)
+        iofa.fa_fwd(q.to(dev), k.to(dev), v.to(dev), o, lse, scale)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle_full(q, k, v, scale)
+        assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"8-wave {dtype} N={N}")
+
+
+@pytest.mark.parametrize("heads", [255, 256])
+def test_fused_wave_form_boundary(heads, dev):
+    # one query tile per head: 255 workgroups take the 4-wave form (255 * 2
+    # workgroups of 128 rows), 256 the 8-wave form; both against the oracle
+    q, k, v = make_qkv(1, heads, 200, 128, "bf16", seed_base=9500 + heads)
+    scale = default_scale(128)
+    _say(f"fused wave-form boundary H={heads}")
+    o, lse = nan_outputs(q, dev)
+    iofa.fa_fwd(q.to(dev), k.to(dev), v.to(dev), o, lse, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"boundary H={heads}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fused_long_heads_every_element(d, dev):
     # heads with more query tiles than an XCD runs at once (48 workgroups of
