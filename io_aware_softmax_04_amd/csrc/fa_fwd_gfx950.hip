@@ -45,16 +45,16 @@
 namespace iofa {
 
 // Waves per workgroup of the 16-bit kernel: 4 (two workgroups per CU) or 8
-// (one).  With 8, all eight waves of a CU share one per-tile barrier and so
-// stay on the same key tile: with two 4-wave workgroups per CU one of them
-// ran ahead of the other (398 to 597 us for the same work at B1 H32 N16384),
-// the workgroups of an XCD drifted apart by up to 3.4 MiB of K and V, and
-// heads whose keys exceed the XCD's L2 were fetched 3.7 times instead of
-// twice.  The launch takes 8 at d = 128 when that still gives every CU a
-// workgroup (measured the same or faster there, B2 H8 N8191 2% faster), and
-// 4 otherwise (at d = 64 8 measured 4% slower at B4 H16 N1024; a grid of
-// fewer 8-wave workgroups than CUs would leave CUs idle).  Both forms do
-// the same arithmetic per wave, so their results are identical.
+// (one).  With 8, all eight waves of a CU share the workgroup's barriers and
+// so stay within two key tiles of each other: with two 4-wave workgroups per
+// CU one of them ran ahead of the other (398 to 597 us for the same work at
+// B1 H32 N16384), the workgroups of an XCD drifted apart by up to 3.4 MiB of
+// K and V, and heads whose keys exceed the XCD's L2 were fetched 3.7 times
+// instead of twice.  The launch takes 8 at d = 128 when that still gives
+// every CU a workgroup (measured the same or faster there, B2 H8 N8191 2%
+// faster), and 4 otherwise (at d = 64 8 measured 4% slower at B4 H16 N1024;
+// a grid of fewer 8-wave workgroups than CUs would leave CUs idle).  Both
+// forms do the same arithmetic per wave, so their results are identical.
 template <int D, int BC, int NW_ = 4>
 struct FusedCfg {
   static constexpr int NW = NW_;          // waves per workgroup
