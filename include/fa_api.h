@@ -33,7 +33,10 @@
  *              is enqueued, and pointers may then be NULL.
  *   Limits     d in {64, 128}; N * d < 2^31; B * H < 2^31; the number of
  *              workgroups < 2^31.  Values are not checked for NaN/Inf.
- *   Threads    Stateless and reentrant; fa_last_error() is per host thread.
+ *   Threads    Reentrant; fa_last_error() is per host thread.  Two entry
+ *              points keep state: fa_fwd_splitkv_noalloc shares one scratch
+ *              array per GPU between its calls (overlapping calls race), and
+ *              fa_softmax_set_wait_limit sets a process-wide bound.
  */
 #ifndef IOFA_FA_API_H
 #define IOFA_FA_API_H
