@@ -211,6 +211,37 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, in
                                   int num_splits);
 
 /*
+ * Split-KV forward for queries and keys of different lengths: Q and O are
+ * (B, H, Nq, d), K and V (B, H, Nk, d), LSE (B, H, Nq); every query row
+ * attends to all Nk key rows of its head.  It serves decode (a few query
+ * rows, often one, against a long key sequence: the case the key-range split
+ * exists for, since the query tiles alone give the chip almost no
+ * workgroups) and attention of one sequence over another.  The definition is
+ * that of fa_fwd with S = scale * Q K^T of shape Nq x Nk; the two passes are
+ * those of fa_fwd_splitkv, with G chosen from the query tiles (for the waves
+ * of pass 1) and the key tiles (for the range lengths).
+ *   Nq = 0 (or B = 0 or H = 0) is an empty call; Nq > 0 with Nk = 0 is
+ *   FA_ERR_SHAPE (a softmax over no keys is undefined).  Both lengths obey
+ *   the limits of fa_fwd.  fa_fwd_splitkv(..., N, ...) is this call with
+ *   Nq = Nk = N.  Other arguments, workspace, results and errors as
+ *   fa_fwd_splitkv, with B*H*Nq rows of partials.
+ */
+int fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      void* workspace, size_t workspace_bytes, int num_splits, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int dtype,
+                      void* stream);
+
+/* The G that fa_fwd_splitkv_qk uses for `requested`; 0 for invalid sizes or
+ * dtype (including Nq or Nk below 1). */
+int fa_splitkv_qk_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
+                             int requested);
+
+/* Workspace bytes fa_fwd_splitkv_qk needs: G * B*H*Nq * (d + 1) * 4 for the
+ * G it resolves, 0 when G = 1 or for invalid arguments. */
+size_t fa_splitkv_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                     int dtype, int num_splits);
+
+/*
  * Merge of num_parts partial attention results over disjoint key sets (the
  * block merge of the special-jiahao.github.io "Flash Attention" note,
  * section "增量求解 softmax", for num_parts blocks), per row r:

@@ -1,7 +1,8 @@
 """Exact-attention forward for MI355X (gfx950): Python binding of the C ABI.
 
 The functions ``fa_fwd``, ``fa_fwd_splitkv``, ``fa_fwd_splitkv_noalloc``,
-``fa_splitkv_num_splits``, ``fa_splitkv_workspace_bytes``, ``fa_merge_partials``,
+``fa_splitkv_num_splits``, ``fa_splitkv_workspace_bytes``, ``fa_fwd_splitkv_qk``,
+``fa_splitkv_qk_num_splits``, ``fa_splitkv_qk_workspace_bytes``, ``fa_merge_partials``,
 ``fa_softmax_rows``, ``fa_softmax_workspace_bytes``, ``fa_softmax_x_reads``,
 ``fa_softmax_set_wait_limit``, ``fa_bwd``, ``fa_bwd_workspace_bytes``,
 ``fa_fwd_fp8``, ``fa_naive_fwd``, ``fa_naive_workspace_bytes``,
@@ -11,8 +12,8 @@ marshal torch tensors into pointers, sizes and the current HIP stream.  Every
 step of the computation runs in the HIP kernels of ``libiofa.so``; there is
 no CPU fallback, and a missing library raises instead of computing.
 
-``forward``, ``forward_splitkv``, ``forward_fp8``, ``backward``, ``softmax`` and
-``naive_forward`` are conveniences that allocate the outputs (and workspaces)
+``forward``, ``forward_splitkv``, ``forward_qk``, ``forward_fp8``, ``backward``,
+``softmax`` and ``naive_forward`` are conveniences that allocate the outputs (and workspaces)
 with torch and call the entry points.
 """
 
@@ -26,7 +27,8 @@ import torch
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "library_path", "load_library",
     "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "FA_NOALLOC_SCRATCH_BYTES",
-    "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes",
+    "fa_splitkv_num_splits", "fa_splitkv_workspace_bytes", "fa_fwd_splitkv_qk",
+    "fa_splitkv_qk_num_splits", "fa_splitkv_qk_workspace_bytes", "forward_qk",
     "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes", "fa_softmax_x_reads",
     "fa_softmax_set_wait_limit", "softmax",
     "fa_bwd", "fa_bwd_workspace_bytes", "backward", "fa_fwd_fp8", "forward_fp8",
@@ -82,6 +84,14 @@ def load_library():
     lib.fa_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_qk.argtypes = [vp, vp, vp, vp, fp, vp, ctypes.c_size_t, ctypes.c_int,
+                                      i64, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.fa_fwd_splitkv_qk.restype = ctypes.c_int
+    lib.fa_splitkv_qk_num_splits.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.fa_splitkv_qk_num_splits.restype = ctypes.c_int
+    lib.fa_splitkv_qk_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                  ctypes.c_int]
+    lib.fa_splitkv_qk_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_merge_partials.argtypes = [fp, fp, ctypes.c_int, i64, i64, vp, fp, ctypes.c_int, vp]
     lib.fa_merge_partials.restype = ctypes.c_int
     lib.fa_softmax_rows.argtypes = [vp, vp, fp, i64, i64, ctypes.c_int, vp, ctypes.c_size_t, vp]
@@ -236,6 +246,47 @@ def fa_fwd_splitkv_noalloc(q, k, v, o, lse, scale, num_splits=0, stream=None):
 
 
 FA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fa_fwd_splitkv_qk(q, k, v, o, lse, workspace, scale, num_splits=0, stream=None):
+    """Split-KV forward for queries and keys of different lengths: q and o
+    (B, H, Nq, d), k and v (B, H, Nk, d), lse (B, H, Nq) fp32; workspace a
+    byte tensor of at least fa_splitkv_qk_workspace_bytes() bytes (may be
+    None when that is 0)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D (B, H, N, d) tensor")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in dtype and device")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, Nq, d = (int(x) for x in q.shape)
+    Nk = int(k.shape[2])
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be (B, H, Nk, d) with q's B, H and d")
+    if tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("o must have q's shape")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be a contiguous fp32 (B, H, Nq) tensor")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_splitkv_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _fptr(lse),
+                                   _ptr(workspace), ws_bytes, int(num_splits), B, H, Nq, Nk, d,
+                                   float(scale), _DTYPE_CODE[q.dtype], _stream(stream, q.device))
+    _check(st)
+
+
+def fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, dtype, requested=0):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, code, int(requested)))
+
+
+def fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits=0):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, code,
+                                                            int(num_splits)))
 
 
 def fa_splitkv_num_splits(B, H, N, d, dtype, requested=0):
@@ -431,6 +482,20 @@ def forward_splitkv(q, k, v, scale=None, num_splits=0, stream=None):
     nbytes = fa_splitkv_workspace_bytes(B, H, N, d, q.dtype, num_splits)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
     fa_fwd_splitkv(q, k, v, o, lse, ws, scale, num_splits, stream)
+    return o, lse
+
+
+def forward_qk(q, k, v, scale=None, num_splits=0, stream=None):
+    """Allocate O, LSE and the workspace and run the split-KV forward for q
+    (B, H, Nq, d) against k, v (B, H, Nk, d).  Returns (o, lse)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, q.dtype, num_splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+    fa_fwd_splitkv_qk(q, k, v, o, lse, ws, scale, num_splits, stream)
     return o, lse
 
 

@@ -78,34 +78,45 @@ struct Region {
   const char* name;
 };
 
-// Shared checks of fa_fwd and fa_naive_fwd.  Returns FA_OK and sets *empty
-// when there is nothing to do.
-int check_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-                 bool lse_required, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                 int dtype, bool* empty) {
+// Shared checks of the forward entry points, for Nq query rows and Nk key
+// rows per head (Nq = Nk = N for self-attention).  Returns FA_OK and sets
+// *empty when there is nothing to do: no query rows (or B or H zero).
+// Queries without keys are refused: their softmax has no terms.
+int check_common_qk(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                    bool lse_required, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    float scale, int dtype, bool* empty) {
   *empty = false;
+  const std::string sizes = Nq == Nk ? " N=" + std::to_string(Nq)
+                                     : " Nq=" + std::to_string(Nq) + " Nk=" + std::to_string(Nk);
   if (elem_bytes(dtype) == 0)
     return fail(FA_ERR_DTYPE, "dtype " + std::to_string(dtype) + " is not FA_F32, FA_F16 or FA_BF16");
-  if (B < 0 || H < 0 || N < 0)
-    return fail(FA_ERR_SHAPE, "B, H and N must be >= 0 (got B=" + std::to_string(B) +
-                                  " H=" + std::to_string(H) + " N=" + std::to_string(N) + ")");
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B, H and the sequence lengths must be >= 0 (got B=" +
+                                  std::to_string(B) + " H=" + std::to_string(H) + sizes + ")");
   if (d != 64 && d != 128)
     return fail(FA_ERR_HEAD_DIM, "head dimension d must be 64 or 128 (got " + std::to_string(d) + ")");
   if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
-  if (B == 0 || H == 0 || N == 0) {
+  if (B == 0 || H == 0 || Nq == 0) {
     *empty = true;
     return FA_OK;
   }
-  if (!within_limits(B, H, N, d))
-    return fail(FA_ERR_SHAPE, "B * H, N * d and B * H * N must each be < 2^31 (got B=" +
-                                  std::to_string(B) + " H=" + std::to_string(H) +
-                                  " N=" + std::to_string(N) + ")");
+  if (Nk == 0) return fail(FA_ERR_SHAPE, "query rows need at least one key row (Nk = 0)");
+  if (!within_limits(B, H, Nq, d) || !within_limits(B, H, Nk, d))
+    return fail(FA_ERR_SHAPE, "B * H, N * d and B * H * N must each be < 2^31 for both lengths "
+                              "(got B=" + std::to_string(B) + " H=" + std::to_string(H) + sizes + ")");
   if (!Q || !K || !V || !O) return fail(FA_ERR_NULL, "Q, K, V and O must not be NULL");
   if (lse_required && !LSE) return fail(FA_ERR_NULL, "LSE must not be NULL");
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
     return fail(FA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
   if (LSE && !aligned(LSE, 4)) return fail(FA_ERR_ALIGN, "LSE must be 4-byte aligned");
   return FA_OK;
+}
+
+// The same checks for one sequence length (fa_fwd, fa_naive_fwd, ...).
+int check_common(const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+                 bool lse_required, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 int dtype, bool* empty) {
+  return check_common_qk(Q, K, V, O, LSE, lse_required, B, H, N, N, d, scale, dtype, empty);
 }
 
 int check_aliasing(const Region* in, int nin, const Region* out, int nout) {
@@ -143,7 +154,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int
   if (st != FA_OK) return st;
   if (iofa::fused_workgroups(dtype, B * H, N, 1) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
-  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
+  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
   return hip_status(iofa::launch_fused(a), "fused forward launch");
 }
 
@@ -176,15 +187,17 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, void* O, float* LSE,
   return hip_status(iofa::launch_fp8(a), "FP8 forward launch");
 }
 
-int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested) {
-  if (elem_bytes(dtype) == 0 || B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  if (!within_limits(B, H, N, d)) return 0;
-  const int64_t tiles = ceil_div(N, iofa::fused_key_tile(dtype, d));
+int fa_splitkv_qk_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
+                             int requested) {
+  if (elem_bytes(dtype) == 0 || B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128))
+    return 0;
+  if (!within_limits(B, H, Nq, d) || !within_limits(B, H, Nk, d)) return 0;
+  const int64_t tiles = ceil_div(Nk, iofa::fused_key_tile(dtype, d));
   const int64_t cap = tiles < kMaxSplits ? tiles : kMaxSplits;
   int64_t g = requested;
   if (g <= 0) {
     // enough waves for one full round of the chip
-    const int64_t per_split = iofa::fused_waves(dtype, B * H, N, 1);
+    const int64_t per_split = iofa::fused_waves(dtype, B * H, Nq, 1);
     g = (kTargetWaves + per_split - 1) / per_split;
     const int64_t longest = tiles / kMinTilesPerSplit;
     if (g > longest) g = longest;
@@ -194,26 +207,37 @@ int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
   return static_cast<int>(g);
 }
 
-size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
-                                  int num_splits) {
-  const int g = fa_splitkv_num_splits(B, H, N, d, dtype, num_splits);
+int fa_splitkv_num_splits(int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int requested) {
+  return fa_splitkv_qk_num_splits(B, H, N, N, d, dtype, requested);
+}
+
+size_t fa_splitkv_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                     int dtype, int num_splits) {
+  const int g = fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, dtype, num_splits);
   if (g <= 1) return 0;
   // g > 1 only for sizes within the limits, so the product fits
-  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N);
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(Nq);
   return static_cast<size_t>(g) * rows * (static_cast<size_t>(d) + 1) * sizeof(float);
 }
 
-int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                   void* workspace, size_t workspace_bytes, int num_splits, int64_t B, int64_t H,
-                   int64_t N, int64_t d, float scale, int dtype, void* stream) {
+size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                                  int num_splits) {
+  return fa_splitkv_qk_workspace_bytes(B, H, N, N, d, dtype, num_splits);
+}
+
+int fa_fwd_splitkv_qk(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      void* workspace, size_t workspace_bytes, int num_splits, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int dtype,
+                      void* stream) {
   g_last_error.clear();
   bool empty = false;
-  int st = check_common(Q, K, V, O, LSE, true, B, H, N, d, scale, dtype, &empty);
+  int st = check_common_qk(Q, K, V, O, LSE, true, B, H, Nq, Nk, d, scale, dtype, &empty);
   if (st != FA_OK || empty) return st;
-  const int g = fa_splitkv_num_splits(B, H, N, d, dtype, num_splits);
-  const size_t tensor = static_cast<size_t>(B * H * N * d) * elem_bytes(dtype);
-  const size_t lse = static_cast<size_t>(B * H * N) * sizeof(float);
-  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits);
+  const int g = fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, dtype, num_splits);
+  const size_t qtensor = static_cast<size_t>(B * H * Nq * d) * elem_bytes(dtype);
+  const size_t ktensor = static_cast<size_t>(B * H * Nk * d) * elem_bytes(dtype);
+  const size_t lse = static_cast<size_t>(B * H * Nq) * sizeof(float);
+  const size_t need = fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
   if (g > 1) {
     if (!workspace) return fail(FA_ERR_NULL, "workspace must not be NULL when splitting");
     if (!aligned(workspace, 16)) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -221,23 +245,31 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* 
       return fail(FA_ERR_SHAPE, "workspace holds " + std::to_string(workspace_bytes) +
                                     " bytes, the split needs " + std::to_string(need));
   }
-  const Region in[3] = {{Q, tensor, "Q"}, {K, tensor, "K"}, {V, tensor, "V"}};
-  const Region out[3] = {{O, tensor, "O"}, {LSE, lse, "LSE"},
+  const Region in[3] = {{Q, qtensor, "Q"}, {K, ktensor, "K"}, {V, ktensor, "V"}};
+  const Region out[3] = {{O, qtensor, "O"}, {LSE, lse, "LSE"},
                          {workspace, g > 1 ? need : 0, "workspace"}};
   st = check_aliasing(in, 3, out, 3);
   if (st != FA_OK) return st;
-  if (iofa::fused_workgroups(dtype, B * H, N, g) >= (int64_t(1) << 31) ||
-      iofa::merge_workgroups(B * H * N, d) >= (int64_t(1) << 31))
+  if (iofa::fused_workgroups(dtype, B * H, Nq, g) >= (int64_t(1) << 31) ||
+      iofa::merge_workgroups(B * H * Nq, d) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
-  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)};
+  iofa::FwdArgs a{Q, K, V, O, LSE, B * H, Nq, Nk, d, scale, dtype,
+                  static_cast<hipStream_t>(stream)};
   if (g == 1) return hip_status(iofa::launch_fused(a), "fused forward launch");
   float* o_part = static_cast<float*>(workspace);
-  float* lse_part = o_part + static_cast<size_t>(g) * B * H * N * d;
+  float* lse_part = o_part + static_cast<size_t>(g) * B * H * Nq * d;
   st = hip_status(iofa::launch_fused_partial(a, g, o_part, lse_part), "split-KV partial launch");
   if (st != FA_OK) return st;
-  iofa::MergeArgs m{o_part, lse_part, g, B * H * N, d, O, LSE, dtype,
+  iofa::MergeArgs m{o_part, lse_part, g, B * H * Nq, d, O, LSE, dtype,
                     static_cast<hipStream_t>(stream)};
   return hip_status(iofa::launch_merge(m), "split-KV merge launch");
+}
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   void* workspace, size_t workspace_bytes, int num_splits, int64_t B, int64_t H,
+                   int64_t N, int64_t d, float scale, int dtype, void* stream) {
+  return fa_fwd_splitkv_qk(Q, K, V, O, LSE, workspace, workspace_bytes, num_splits, B, H, N, N,
+                           d, scale, dtype, stream);
 }
 
 static_assert(FA_NOALLOC_SCRATCH_BYTES == iofa::kScratchBytes,
@@ -318,7 +350,7 @@ int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
   if (st != FA_OK) return st;
   if (iofa::naive_max_workgroups(dtype, B * H, N) >= (int64_t(1) << 31))
     return fail(FA_ERR_SHAPE, "too many workgroups");
-  iofa::NaiveArgs a{{Q, K, V, O, LSE, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream)},
+  iofa::NaiveArgs a{{Q, K, V, O, LSE, B * H, N, N, d, scale, dtype, static_cast<hipStream_t>(stream)},
                     S_ws, P_ws, round_up8(N)};
   return hip_status(iofa::launch_naive(a), "naive forward launch");
 }
@@ -447,6 +479,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_version(void) { return 300; }
+int fa_version(void) { return 400; }
 
 }  // extern "C"

@@ -321,6 +321,8 @@ struct WaveState {
 // copy (read in j-2, copy in j); one barrier per tile measured 2.2-2.7%
 // slower at B2 H16 N4096, B2 H8 N8191 and B1 H32 N16384, bit-identical.
 //
+// Q and O hold Nq rows per head, K and V Nk (the same except for attention
+// of one sequence of queries over another of keys, decode included).
 // With PARTIAL the workgroup covers only the keys of its split (key_range)
 // and writes the normalised partial output in fp32 to Out[(split*BH + bh),
 // q, :] and its log-sum-exp to Lse[(split*BH + bh), q]; the partials are
@@ -330,7 +332,7 @@ template <class T, int D, int BC, bool PARTIAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ Out,
-    float* __restrict__ Lse, int N, int BH, int num_qtiles, int num_splits, int num_wg,
+    float* __restrict__ Lse, int Nq, int Nk, int BH, int num_qtiles, int num_splits, int num_wg,
     float scale) {
   using C = FusedCfg<D, BC, NW>;
   using vec8 = typename T::vec8;
@@ -345,12 +347,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
 
   const GridPos gp = grid_pos(num_qtiles, num_splits, num_wg);
   const int bh = gp.bh, qt = gp.qt;
-  const int2 kr = key_range(N, BC, gp.split, num_splits);
+  const int2 kr = key_range(Nk, BC, gp.split, num_splits);
   const int NK = kr.y;                 // keys of this workgroup
-  const size_t head = static_cast<size_t>(bh) * N * D;
+  const size_t head = static_cast<size_t>(bh) * Nq * D;    // Q and O rows of this head
+  const size_t khead = static_cast<size_t>(bh) * Nk * D;   // K and V rows of this head
   const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head + static_cast<size_t>(kr.x) * D;
-  const uint16_t* Vh = V + head + static_cast<size_t>(kr.x) * D;
+  const uint16_t* Kh = K + khead + static_cast<size_t>(kr.x) * D;
+  const uint16_t* Vh = V + khead + static_cast<size_t>(kr.x) * D;
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (q < N) w = *reinterpret_cast<const u32x4*>(Qh + static_cast<size_t>(q) * D + 16 * kk + 8 * ws.hi);
+    if (q < Nq) w = *reinterpret_cast<const u32x4*>(Qh + static_cast<size_t>(q) * D + 16 * kk + 8 * ws.hi);
     w ^= flip;
     ws.qf[kk] = __builtin_bit_cast(vec8, w);
   }
@@ -491,12 +494,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   // a7: O = acc / l rounded to the input type (or kept fp32 for a partial);
   // LSE = ln2 * (m + log2 l).  Lane half hi holds columns 32*cb + 8*g + 4*hi
   // + 0..3 in registers 4*g .. 4*g+3.
-  if (q < N) {
+  if (q < Nq) {
     const float l = halfwave_sum(ws.l_run);
     const float inv_l = 1.0f / l;
     const float lse = (ws.m_run + __builtin_amdgcn_logf(l)) * kLn2;
     if constexpr (PARTIAL) {
-      const size_t row = (static_cast<size_t>(gp.split) * BH + bh) * N + q;
+      const size_t row = (static_cast<size_t>(gp.split) * BH + bh) * Nq + q;
       float* Oq = static_cast<float*>(Out) + row * D;
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb)
@@ -518,7 +521,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
           *reinterpret_cast<u32x2*>(Oq + 32 * cb + 8 * g + 4 * ws.hi) = w;
         }
       }
-      if (ws.hi == 0) Lse[static_cast<size_t>(bh) * N + q] = lse;
+      if (ws.hi == 0) Lse[static_cast<size_t>(bh) * Nq + q] = lse;
     }
   }
 }
@@ -537,7 +540,7 @@ template <int D, bool PARTIAL>
 __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K,
     const float* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
-    int N, int BH, int num_qtiles, int num_splits, int num_wg, float scale) {
+    int Nq, int Nk, int BH, int num_qtiles, int num_splits, int num_wg, float scale) {
   constexpr int QPB = 32, TPQ = 8, DPT = D / TPQ, BC = 32, LS = D + 4;
   __shared__ __attribute__((aligned(16))) float Ks[BC * LS];
   __shared__ __attribute__((aligned(16))) float Vs[BC * LS];
@@ -545,9 +548,10 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
   const int tid = threadIdx.x;
   const GridPos gp = grid_pos(num_qtiles, num_splits, num_wg);
   const int bh = gp.bh, qt = gp.qt;
-  const int2 kr = key_range(N, BC, gp.split, num_splits);
+  const int2 kr = key_range(Nk, BC, gp.split, num_splits);
   const int kbeg = kr.x, kend = kr.x + kr.y;
-  const size_t head = static_cast<size_t>(bh) * N * D;
+  const size_t head = static_cast<size_t>(bh) * Nq * D;    // Q and O rows of this head
+  const size_t khead = static_cast<size_t>(bh) * Nk * D;   // K and V rows of this head
   const int qi = tid / TPQ, part = tid % TPQ;
   const int q = qt * QPB + qi;
   const int c0 = part * DPT;
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
   float qv[DPT], ov[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) {
-    qv[e] = (q < N) ? Q[head + static_cast<size_t>(q) * D + c0 + e] : 0.f;
+    qv[e] = (q < Nq) ? Q[head + static_cast<size_t>(q) * D + c0 + e] : 0.f;
     ov[e] = 0.f;
   }
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -565,8 +569,8 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
       const int row = i / (D / 4), c4 = i % (D / 4);
       float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
       if (k0 + row < kend) {
-        kv = *reinterpret_cast<const float4*>(K + head + static_cast<size_t>(k0 + row) * D + 4 * c4);
-        vv = *reinterpret_cast<const float4*>(V + head + static_cast<size_t>(k0 + row) * D + 4 * c4);
+        kv = *reinterpret_cast<const float4*>(K + khead + static_cast<size_t>(k0 + row) * D + 4 * c4);
+        vv = *reinterpret_cast<const float4*>(V + khead + static_cast<size_t>(k0 + row) * D + 4 * c4);
       }
       *reinterpret_cast<float4*>(Ks + row * LS + 4 * c4) = kv;
       *reinterpret_cast<float4*>(Vs + row * LS + 4 * c4) = vv;
@@ -607,9 +611,9 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(
     __syncthreads();
   }
 
-  if (q < N) {
-    const size_t row = PARTIAL ? (static_cast<size_t>(gp.split) * BH + bh) * N + q
-                               : static_cast<size_t>(bh) * N + q;
+  if (q < Nq) {
+    const size_t row = PARTIAL ? (static_cast<size_t>(gp.split) * BH + bh) * Nq + q
+                               : static_cast<size_t>(bh) * Nq + q;
 #pragma unroll
     for (int e = 0; e < DPT; ++e) O[row * D + c0 + e] = ov[e] / l_run;
     if (part == 0) LSE[row] = m_run + logf(l_run);
@@ -660,7 +664,7 @@ static hipError_t launch16_nw(const FwdArgs& a, int splits, void* out, float* ls
   hipLaunchKernelGGL((fa_fwd_16_kernel<T, D, BC, PARTIAL, NW>), dim3(static_cast<unsigned>(wg)),
                      dim3(64 * NW), 0, a.stream, static_cast<const uint16_t*>(a.Q),
                      static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), out, lse,
-                     static_cast<int>(a.N), static_cast<int>(a.BH), qtiles, splits,
+                     static_cast<int>(a.N), static_cast<int>(a.Nk), static_cast<int>(a.BH), qtiles, splits,
                      static_cast<int>(wg), a.scale);
   return hipGetLastError();
 }
@@ -682,7 +686,8 @@ static hipError_t launch32(const FwdArgs& a, int splits, float* out, float* lse)
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, PARTIAL>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
                      a.stream, static_cast<const float*>(a.Q), static_cast<const float*>(a.K),
                      static_cast<const float*>(a.V), out, lse, static_cast<int>(a.N),
-                     static_cast<int>(a.BH), qtiles, splits, static_cast<int>(wg), a.scale);
+                     static_cast<int>(a.Nk), static_cast<int>(a.BH), qtiles, splits,
+                     static_cast<int>(wg), a.scale);
   return hipGetLastError();
 }
 

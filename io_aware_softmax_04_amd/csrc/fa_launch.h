@@ -20,7 +20,8 @@ struct FwdArgs {
   void* O;
   float* LSE;
   int64_t BH;  // B * H
-  int64_t N;
+  int64_t N;   // query rows per head (Q, O, LSE)
+  int64_t Nk;  // key rows per head (K, V): N itself for self-attention
   int64_t d;
   float scale;
   int dtype;

@@ -40,9 +40,10 @@ void check_launch(bool ok, const char* what) {
 }
 
 bool fwd_ok(const iofa::FwdArgs& a) {
-  return a.Q && a.K && a.V && a.O && a.BH >= 1 && a.N >= 1 && (a.d == 64 || a.d == 128) &&
-         a.dtype >= 0 && a.dtype <= 2 && std::isfinite(a.scale) && a.BH * a.N < (int64_t(1) << 31) &&
-         a.N * a.d < (int64_t(1) << 31);
+  return a.Q && a.K && a.V && a.O && a.BH >= 1 && a.N >= 1 && a.Nk >= 1 &&
+         (a.d == 64 || a.d == 128) && a.dtype >= 0 && a.dtype <= 2 && std::isfinite(a.scale) &&
+         a.BH * a.N < (int64_t(1) << 31) && a.N * a.d < (int64_t(1) << 31) &&
+         a.BH * a.Nk < (int64_t(1) << 31) && a.Nk * a.d < (int64_t(1) << 31);
 }
 
 }  // namespace
@@ -201,6 +202,33 @@ int main() {
                       shape_ok && is_empty(B, H, N) && pk != 3, "fa_fwd_fp8");
                 (void)fa_naive_workspace_bytes(B, H, N, dt);
               }
+  // the split-KV forward over queries and keys of different lengths
+  for (int64_t B : kBig)
+    for (int64_t H : {int64_t(1), int64_t(3)})
+      for (int64_t Nq : kBig)
+        for (int64_t Nk : kBig)
+          for (int64_t d : kD)
+            for (int dt : kDtype)
+              for (float sc : {0.125f, std::numeric_limits<float>::infinity()})
+                for (int pk : {0, 2, 3}) {
+                  const Ptrs p = ptrs(pk);
+                  std::snprintf(g_case, sizeof(g_case),
+                                "qk B=%lld H=%lld Nq=%lld Nk=%lld d=%lld dtype=%d scale=%g "
+                                "pointers=%d",
+                                static_cast<long long>(B), static_cast<long long>(H),
+                                static_cast<long long>(Nq), static_cast<long long>(Nk),
+                                static_cast<long long>(d), dt, static_cast<double>(sc), pk);
+                  const bool empty = B >= 0 && Nq >= 0 && Nk >= 0 && (d == 64 || d == 128) &&
+                                     std::isfinite(sc) && dt >= 0 && dt <= 2 &&
+                                     (B == 0 || Nq == 0);
+                  for (int g : {0, 4}) {
+                    const size_t need = fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, dt, g);
+                    (void)fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, dt, g);
+                    after(fa_fwd_splitkv_qk(p.q, p.k, p.v, p.o, p.lse, p.ws, need, g, B, H, Nq,
+                                            Nk, d, sc, dt, nullptr),
+                          empty, "fa_fwd_splitkv_qk");
+                  }
+                }
   // merge and softmax over their own arguments
   for (int64_t rows : kBig)
     for (int64_t d : kD)

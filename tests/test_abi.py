@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_splitkv_num_splits",
-        "fa_splitkv_workspace_bytes",
+        "fa_splitkv_workspace_bytes", "fa_fwd_splitkv_qk", "fa_splitkv_qk_num_splits",
+        "fa_splitkv_qk_workspace_bytes",
         "fa_merge_partials", "fa_softmax_rows", "fa_softmax_workspace_bytes",
         "fa_softmax_x_reads", "fa_softmax_set_wait_limit", "fa_bwd",
         "fa_bwd_workspace_bytes", "fa_fwd_fp8", "fa_naive_fwd",
@@ -51,7 +52,7 @@ def test_symbols_have_c_linkage():
 
 
 def test_status_strings_and_version(lib):
-    assert iofa.fa_version() == 300
+    assert iofa.fa_version() == 400
     assert iofa.fa_status_string(0) == "ok"
     for s in range(1, 9):
         assert iofa.fa_status_string(s) not in ("ok", "unknown status")
@@ -191,6 +192,50 @@ def test_splitkv_rejects_bad_arguments(lib, kw, status):
 
 def test_splitkv_empty_problem(lib):
     assert splitkv(lib, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, N=0) == 0
+
+
+def splitkv_qk(lib, ws=WS, ws_bytes=1 << 30, splits=4, lse=L, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, B=2, H=2, Nq=1, Nk=4096, d=128, scale=0.1, dtype=2)
+    args.update(kw)
+    lse_p = ctypes.cast(ctypes.c_void_p(lse), ctypes.POINTER(ctypes.c_float)) if lse else None
+    return lib.fa_fwd_splitkv_qk(*(ctypes.c_void_p(args[x]) for x in "qkvo"), lse_p,
+                                 ctypes.c_void_p(ws), ws_bytes, splits, args["B"], args["H"],
+                                 args["Nq"], args["Nk"], args["d"], args["scale"], args["dtype"],
+                                 None)
+
+
+def test_split_count_policy_for_queries_and_keys_of_different_lengths(lib):
+    # equal lengths: the same G as fa_splitkv_num_splits
+    for B, H, N, d in ((2, 2, 4096, 128), (2, 16, 4096, 128), (4, 2, 1024, 128), (1, 1, 300, 64)):
+        assert (iofa.fa_splitkv_qk_num_splits(B, H, N, N, d, 2, 0)
+                == iofa.fa_splitkv_num_splits(B, H, N, d, 2, 0))
+    # decode at B2 H16: one 4-wave query tile per head (128 waves), so 16
+    # ranges would reach 2048 waves; 128 key tiles allow 8 of at least 16
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 4096, 128, 2, 0) == 8
+    # one head decoding 16384 keys: 512 key tiles, 32 ranges of 16
+    assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 16384, 128, 2, 0) == 32
+    # the cap follows the key tiles, not the query rows
+    assert iofa.fa_splitkv_qk_num_splits(1, 1, 5000, 100, 128, 2, 99) == 4
+    assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 0, 128, 2, 0) == 0     # no keys
+    assert iofa.fa_splitkv_qk_num_splits(1, 1, 0, 100, 128, 2, 0) == 0   # no queries
+    assert iofa.fa_splitkv_qk_workspace_bytes(2, 16, 1, 4096, 128, 2, 0) == 8 * 32 * 1 * 129 * 4
+    assert iofa.fa_splitkv_qk_workspace_bytes(2, 16, 1, 4096, 128, 2, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nk=0), 2), (dict(Nk=-1), 2), (dict(Nq=-1), 2), (dict(Nk=1 << 24), 2),
+    (dict(ws=0), 1), (dict(ws_bytes=100), 2), (dict(lse=0), 1), (dict(d=96), 3),
+    (dict(o=K + (1 << 20)), 7),          # O inside K's (B, H, Nk, d) extent
+    (dict(k=O + 512), 7),                # K starts inside O's (B, H, Nq, d) extent
+])
+def test_splitkv_qk_rejects_bad_arguments(lib, kw, status):
+    st = splitkv_qk(lib, **kw)
+    assert st == status, (kw, st, iofa.fa_last_error())
+    assert iofa.fa_last_error() != ""
+
+
+def test_splitkv_qk_without_queries_is_empty(lib):
+    assert splitkv_qk(lib, q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, Nq=0) == 0
 
 
 def merge(lib, op=Q, lp=K, g=3, rows=10, d=64, o=O, lse=L, dtype=2):

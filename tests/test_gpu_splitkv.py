@@ -8,7 +8,8 @@ import torch
 
 import io_aware_softmax_04_amd as iofa
 import oracle
-from helpers import TOL, assert_parity, errors, oracle_full, oracle_rows, sample_rows, widen
+from helpers import (TOL, assert_parity, errors, nan_outputs, oracle_full, oracle_rows,
+                     sample_rows, widen)
 from workloads import default_scale, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +99,74 @@ def test_splitkv_partials_match_partial_attention(dtype, d, dev):
         assert np.abs(lse_part[s] - pl).max() <= tol["lse_abs"], s
     o_ref, lse_ref = oracle_full(q, k, v, scale)
     assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, q.dtype, f"splitkv {dtype} d={d} G=3")
+
+
+# Queries and keys of different lengths: q (B, H, Nq, d) against k, v
+# (B, H, Nk, d).  The oracle is the attention definition over all Nk keys
+# (oracle.partial_attention over the whole key range).  Decode (Nq = 1) with
+# short, ragged and long key sequences, and one sequence over another, both
+# shorter and longer.
+QK_SHAPES = [(1, 1), (1, 33), (1, 1000), (1, 4097), (3, 700), (300, 1000), (1000, 77), (129, 4096)]
+
+
+def _qk_inputs(B, H, Nq, Nk, d, dtype, seed):
+    q, _, _ = make_qkv(B, H, Nq, d, dtype, seed_base=seed)
+    _, k, v = make_qkv(B, H, Nk, d, dtype, seed_base=seed + 7919)
+    return q, k, v
+
+
+def _run_qk(q, k, v, scale, splits, dev):
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = nan_outputs(q, dev)
+    nbytes = iofa.fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, q.dtype, splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev) if nbytes else None
+    iofa.fa_fwd_splitkv_qk(qd, kd, vd, o, lse, ws, scale, splits)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv_qk_matches_oracle(dtype, d, dev):
+    B, H = 2, 3
+    scale = default_scale(d)
+    for Nq, Nk in QK_SHAPES:
+        q, k, v = _qk_inputs(B, H, Nq, Nk, d, dtype, 101 * Nq + Nk + d)
+        po, pl = oracle.partial_attention(widen(q), widen(k), widen(v),
+                                          float(np.float32(scale)), 0, Nk)
+        for splits in (0, 1, 3):
+            g = iofa.fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, q.dtype, splits)
+            _say(f"splitkv qk {dtype} d={d} Nq={Nq} Nk={Nk} requested={splits} G={g}")
+            o, lse = _run_qk(q, k, v, scale, splits, dev)
+            assert_parity(o, lse, po, pl, q.dtype, f"qk {dtype} d={d} Nq={Nq} Nk={Nk} G={g}")
+
+
+def test_splitkv_qk_decode_at_the_benchmarked_size(dev):
+    # one query row per head against the 4096 keys of B2 H16 d128: every
+    # element of O and LSE against the oracle
+    B, H, Nq, Nk, d = 2, 16, 1, 4096, 128
+    q, k, v = _qk_inputs(B, H, Nq, Nk, d, "bf16", 6060)
+    scale = default_scale(d)
+    g = iofa.fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, q.dtype, 0)
+    assert g == 8
+    o, lse = _run_qk(q, k, v, scale, 0, dev)
+    po, pl = oracle.partial_attention(widen(q), widen(k), widen(v), float(np.float32(scale)), 0, Nk)
+    res = assert_parity(o, lse, po, pl, q.dtype, "decode B2 H16 Nk4096 G=8")
+    _say(f"  max_abs={res[0]:.3e} rel_f={res[1]:.3e} lse={res[2]:.3e}")
+
+
+def test_splitkv_qk_with_equal_lengths_is_splitkv(dev):
+    # Nq = Nk: the same launches as fa_fwd_splitkv, so the same bits
+    q, k, v = make_qkv(1, 2, 1000, 128, "bf16", seed_base=808)
+    scale = default_scale(128)
+    for splits in (0, 1, 4):
+        o1, l1 = _run_qk(q, k, v, scale, splits, dev)
+        o2, l2 = iofa.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), scale, splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.cpu().view(torch.int16))
+        assert torch.equal(l1, l2.cpu())
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16, torch.float16])
