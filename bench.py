@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--no-naive", action="store_true", help="skip the naive contrast")
     p.add_argument("--no-splitkv", action="store_true", help="skip the split-KV contrast")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     p.add_argument("--no-softmax", action="store_true", help="skip the row-softmax measurement")
     p.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward measurement")
@@ -321,8 +322,8 @@ def summarise_trace(trace_dir, index, spec, bench_args, out_dir=None):
 BENCH_STDOUT = "bench_stdout.txt"
 
 # the traffic passes run the fused and the naive paths only, a few launches each
-TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-softmax --no-backward --no-fp8 "
-                      "--no-ceiling --no-cpu-baseline")
+TRAFFIC_BENCH_ARGS = ("--steps 3 --warmup 1 --no-splitkv --no-decode --no-softmax --no-backward "
+                      "--no-fp8 --no-ceiling --no-cpu-baseline")
 # Shader counters, in rocprofv3 --pmc passes of at most 8 SQ counters each
 # (a and b for every kernel; c, the LDS pass, optional)
 SQ_PASSES = {
@@ -340,7 +341,8 @@ SHADER_ENGINES = 32          # 8 XCDs x 4 shader engines
 SIMDS = 1024                 # 256 CUs x 4
 # Kernels the counter summary covers: (name filter, FLOPs per MFMA instruction,
 # bench.py arguments of the counter passes, file tag, rocprofv3 kernel regex)
-_SQ_COMMON = "--warmup 100 --no-naive --no-splitkv --no-softmax --no-ceiling --no-cpu-baseline"
+_SQ_COMMON = ("--warmup 100 --no-naive --no-splitkv --no-decode --no-softmax --no-ceiling "
+              "--no-cpu-baseline")
 SQ_KERNELS = {
     "fused": ("fused", 32768.0, f"--steps 20 {_SQ_COMMON} --no-backward --no-fp8", "fused_fwd",
               "fa_fwd_16_kernel"),
@@ -718,6 +720,40 @@ def splitkv_contrast(spec, args, torch, iofa, dev):
     }
 
 
+def decode_measure(spec, torch, iofa, dev):
+    """Decode on the workload's heads: one query row per head against its N
+    keys (B, H, d and dtype of the workload), through the split-KV forward
+    for queries and keys of different lengths.  Bound by HBM: algorithmic
+    bytes are K and V read once, Q read and O, LSE written; the partials'
+    round trip through the workspace is reported beside them."""
+    from workloads import make_qkv
+    B, H, Nk, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    Nq = 1
+    q = make_qkv(B, H, Nq, d, spec["dtype"], seed_base=5151)[0].to(dev)
+    _, k, v = (t.to(dev) for t in make_qkv(B, H, Nk, d, spec["dtype"], seed_base=5252))
+    scale = iofa.default_scale(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    g = iofa.fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, q.dtype, 0)
+    nbytes = iofa.fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, q.dtype, g)
+    ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+    ms = time_graph(lambda: iofa.fa_fwd_splitkv_qk(q, k, v, o, lse, ws, scale, g), torch)
+    e = q.element_size()
+    alg = e * B * H * (2 * Nk * d + 2 * Nq * d) + 4 * B * H * Nq
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {
+        "workload": (f"{spec['dtype']} B{B} H{H} Nq{Nq} Nk{Nk} d{d} "
+                     "(decode: one query row per head)"),
+        "num_splits": g,
+        "timing": "20 calls captured in a graph, replayed 10 times between two events",
+        "ms": round(ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": alg},
+        "partials_round_trip_bytes": 2 * nbytes,
+    }
+
+
 def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
     """The backward pass on the same workload.  TFLOP/s on the algorithmic
     count 10*B*H*N^2*d (the five N^2 d products a single pass needs, 2.5x the
@@ -957,6 +993,10 @@ def main():
     if not args.no_splitkv and spec["dtype"] != "fp32":
         line["splitkv_contrast"] = splitkv_contrast(spec, args, torch, iofa, dev)
         print(f"[bench] split-KV: {line['splitkv_contrast']}", file=sys.stderr, flush=True)
+
+    if not args.no_decode and spec["dtype"] != "fp32":
+        line["decode"] = decode_measure(spec, torch, iofa, dev)
+        print(f"[bench] decode: {line['decode']}", file=sys.stderr, flush=True)
 
     if not args.no_backward and spec["dtype"] != "fp32":
         line["backward"] = backward_measure(q, k, v, scale, spec, args, torch, iofa, dev)

@@ -69,6 +69,11 @@ bool within_limits(int64_t B, int64_t H, int64_t N, int64_t d) {
 // the merge than the extra workgroups win back).
 constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kTargetWaves = 2048;   // 8 per CU on 256 CUs
+// With fewer query rows than one query tile (decode) every workgroup is
+// bound by its stream of keys and values: one 4-wave workgroup per CU
+// measured fastest (B1 H8 Nq1 Nk32768: 38 us against 53 us at 2048 waves;
+// B1 H32 Nq1 Nk16384: 55 against 62 us).
+constexpr int64_t kTargetWavesShortQueries = 1024;
 constexpr int64_t kMinTilesPerSplit = 16;
 constexpr int kMaxMergeParts = 4096;
 
@@ -198,7 +203,9 @@ int fa_splitkv_qk_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
   if (g <= 0) {
     // enough waves for one full round of the chip
     const int64_t per_split = iofa::fused_waves(dtype, B * H, Nq, 1);
-    g = (kTargetWaves + per_split - 1) / per_split;
+    const int64_t target = Nq < iofa::fused_query_tile(dtype) ? kTargetWavesShortQueries
+                                                              : kTargetWaves;
+    g = (target + per_split - 1) / per_split;
     const int64_t longest = tiles / kMinTilesPerSplit;
     if (g > longest) g = longest;
   }

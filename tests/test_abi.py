@@ -214,6 +214,10 @@ def test_split_count_policy_for_queries_and_keys_of_different_lengths(lib):
     assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 4096, 128, 2, 0) == 8
     # one head decoding 16384 keys: 512 key tiles, 32 ranges of 16
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 16384, 128, 2, 0) == 32
+    # fewer query rows than one tile: about 1024 waves (one 4-wave workgroup
+    # per CU), so 8 heads of one row take 32 ranges, not 64
+    assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 32768, 128, 2, 0) == 32
+    assert iofa.fa_splitkv_qk_num_splits(1, 32, 1, 16384, 128, 2, 0) == 8
     # the cap follows the key tiles, not the query rows
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 5000, 100, 128, 2, 99) == 4
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 0, 128, 2, 0) == 0     # no keys
