@@ -69,6 +69,22 @@ def test_splitkv_forward_in_a_graph(dev):
                    [o, lse], dev)
 
 
+@pytest.mark.parametrize("Nq,Nk", [(1, 3000), (130, 700)])
+def test_splitkv_qk_forward_in_a_graph(Nq, Nk, dev):
+    # queries and keys of different lengths: one decode row, and a query
+    # block longer than the key sequence
+    q, _, _ = make_qkv(1, 3, Nq, 128, "bf16", seed_base=36)
+    _, k, v = make_qkv(1, 3, Nk, 128, "bf16", seed_base=37)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 3, Nq), dtype=torch.float32, device=dev)
+    g = iofa.fa_splitkv_qk_num_splits(1, 3, Nq, Nk, 128, q.dtype)
+    nbytes = iofa.fa_splitkv_qk_workspace_bytes(1, 3, Nq, Nk, 128, q.dtype, g)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _replays_match(lambda: iofa.fa_fwd_splitkv_qk(q, k, v, o, lse, ws, default_scale(128), g),
+                   [o, lse], dev)
+
+
 def test_backward_in_a_graph(dev):
     q, k, v = (t.to(dev) for t in make_qkv(1, 2, 700, 128, "bf16", seed_base=33))
     do = torch.randn_like(q)
