@@ -53,8 +53,12 @@ namespace iofa {
 // instead of twice.  The launch takes 8 at d = 128 when that still gives
 // every CU a workgroup (measured the same or faster there, B2 H8 N8191 2%
 // faster), and 4 otherwise (at d = 64 8 measured 4% slower at B4 H16 N1024;
-// a grid of fewer 8-wave workgroups than CUs would leave CUs idle).  Both
-// forms do the same arithmetic per wave, so their results are identical.
+// a grid of fewer 8-wave workgroups than CUs would leave CUs idle).  Queries
+// shorter than one 4-wave tile (decode) also take 4: the workgroup is then
+// bound by its stream of keys and values, and the same number of 4-wave
+// workgroups measured 12-23% faster there (B8 H32 Nq1 Nk8192 182 against
+// 236 us).  Both forms do the same arithmetic per wave, so their results are
+// identical.
 template <int D, int BC, int NW_ = 4>
 struct FusedCfg {
   static constexpr int NW = NW_;          // waves per workgroup
@@ -392,104 +396,128 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   __syncthreads();
   f32x16 sa[C::SB], sb[C::SB];
   vec8 pa[C::KSTEPS], pb[C::KSTEPS];
-  ws.template scores<0>(sa);
+  // A wave whose 32 query rows all lie past the last query row (a query
+  // block shorter than the workgroup's, one decode row per head above all)
+  // computes nothing: it issues its share of every K and V copy and joins
+  // every wait and barrier in the same order as the computing waves, which
+  // run the same program below with IDLE false.
+  const bool idle_wave = qt * C::BR + wave * 32 >= Nq;   // wave-uniform
+  auto body = [&](auto idle_c) {
+    constexpr bool IDLE = decltype(idle_c)::value;
+    if constexpr (!IDLE) ws.template scores<0>(sa);
 
-  constexpr int NM = 2 * (D / 16) * C::SB;          // products per iteration
-  constexpr int NRD = (D / 16) * C::SB + 2 * NM / 2;  // K reads + 2 per P V product
-  // LDS reads issued ahead of the interleaved products: at d = 128 kept 4
-  // ahead for the whole tile (1.1-1.4% faster at B2 H16 N4096 and B2 H8
-  // N8191 than 6 ahead with the lead draining over the tile); 8 at d = 64
-  constexpr int LEAD = D == 128 ? 4 : 8;
-  auto bottom = [&](float alpha) {
-    ws.rescale(alpha);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-  // one full iteration j with parity P (compile-time)
-  auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
-                       vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
-    constexpr int P = decltype(par)::value;   // j % 4
-    // raised issue priority from the copies through the products; dropped
-    // again before the wait and barrier (measured 0.8% faster at d = 128,
-    // 3.8% at d = 64, bit-identical output)
-    __builtin_amdgcn_s_setprio(1);
-    kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
-    vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
-    const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
-    ws.template pv_scores<(P + 3) % 4, (P + 1) % 4>(p_prev, s_nxt);
-    // d = 128 keeps its reads LEAD ahead for the whole tile, with three
-    // vector instructions per product (four: 1.1-1.5% slower at B2 H16
-    // N4096, B2 H8 N8191 and B1 H32 N16384; two: 0.5% slower); at d = 64 the
-    // draining order with four measured faster (21.0 vs 21.7 us at
-    // B4 H16 N1024)
-    if constexpr (D == 128)
-      interleave_mfma_valu_lead<NM, NRD, LEAD, 3>();
-    else
-      interleave_mfma_valu<NM, NRD, LEAD, 4>();
-    // the redo decision is wave-uniform, so the accepted path (almost every
-    // tile) carries no rescale factor and no rescale test
-    float alpha;
-    if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
-    __builtin_amdgcn_s_setprio(0);
-    if constexpr (P % 2 == 1) {
+    constexpr int NM = 2 * (D / 16) * C::SB;          // products per iteration
+    constexpr int NRD = (D / 16) * C::SB + 2 * NM / 2;  // K reads + 2 per P V product
+    // LDS reads issued ahead of the interleaved products: at d = 128 kept 4
+    // ahead for the whole tile (1.1-1.4% faster at B2 H16 N4096 and B2 H8
+    // N8191 than 6 ahead with the lead draining over the tile); 8 at d = 64
+    constexpr int LEAD = D == 128 ? 4 : 8;
+    auto bottom = [&](float alpha) {
+      if constexpr (!IDLE) ws.rescale(alpha);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-    }
-  };
-  // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
-  auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
-                  vec8 (&p_cur)[C::KSTEPS]) {
-    constexpr int P = decltype(par)::value;   // j % 4
-    const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
-                               : ws.template softmax<false>(s_cur, p_cur, c2, BC);
-    if (j > 0) ws.template pv<(P + 3) % 4>(p_prev);
-    bottom(alpha);
-    ws.template pv<P>(p_cur);
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
+    };
+    // one full iteration j with parity P (compile-time)
+    auto iteration = [&](auto par, int j, f32x16 (&s_cur)[C::SB], f32x16 (&s_nxt)[C::SB],
+                         vec8 (&p_prev)[C::KSTEPS], vec8 (&p_cur)[C::KSTEPS]) {
+      constexpr int P = decltype(par)::value;   // j % 4
+      if constexpr (IDLE) {
+        kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
+        vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
+      } else {
+        // raised issue priority from the copies through the products; dropped
+        // again before the wait and barrier (measured 0.8% faster at d = 128,
+        // 3.8% at d = 64, bit-identical output)
+        __builtin_amdgcn_s_setprio(1);
+        kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
+        vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
+        const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
+        ws.template pv_scores<(P + 3) % 4, (P + 1) % 4>(p_prev, s_nxt);
+        // d = 128 keeps its reads LEAD ahead for the whole tile, with three
+        // vector instructions per product (four: 1.1-1.5% slower at B2 H16
+        // N4096, B2 H8 N8191 and B1 H32 N16384; two: 0.5% slower); at d = 64 the
+        // draining order with four measured faster (21.0 vs 21.7 us at
+        // B4 H16 N1024)
+        if constexpr (D == 128)
+          interleave_mfma_valu_lead<NM, NRD, LEAD, 3>();
+        else
+          interleave_mfma_valu<NM, NRD, LEAD, 4>();
+        // the redo decision is wave-uniform, so the accepted path (almost every
+        // tile) carries no rescale factor and no rescale test
+        float alpha;
+        if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if constexpr (P % 2 == 1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    };
+    // the last iteration j = NT-1 (parity P): no scores, maybe a ragged tile
+    auto last = [&](auto par, int j, f32x16 (&s_cur)[C::SB], vec8 (&p_prev)[C::KSTEPS],
+                    vec8 (&p_cur)[C::KSTEPS]) {
+      constexpr int P = decltype(par)::value;   // j % 4
+      if constexpr (IDLE) {
+        bottom(0.f);
+      } else {
+        const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
+                                   : ws.template softmax<false>(s_cur, p_cur, c2, BC);
+        if (j > 0) ws.template pv<(P + 3) % 4>(p_prev);
+        bottom(alpha);
+        ws.template pv<P>(p_cur);
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
 
-  if (NT == 1) {
-    last(P0{}, 0, sa, pb, pa);
-  } else {
-    // iteration 0: softmax_0 with scores_1
-    kcp.copy(Kh, 3 * BC, NK, kst[3]);
-    vcp.copy(Vh, BC, NK, vst[1]);
-    {
-      const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
-      ws.template scores<1>(sb);
-      constexpr int NS1 = (D / 16) * C::SB;
-      interleave_mfma_valu<NS1, NS1, 2, 4>();
-      bottom(alpha);
-    }
-    // iterations 1 .. NT-2, four per trip so register sets alternate and
-    // every stage index is a constant
-    int j = 1;
-    for (; j + 3 < NT - 1; j += 4) {
-      iteration(P1{}, j, sb, sa, pa, pb);
-      iteration(P2{}, j + 1, sa, sb, pb, pa);
-      iteration(P3{}, j + 2, sb, sa, pa, pb);
-      iteration(P0{}, j + 3, sa, sb, pb, pa);
-    }
-    if (j < NT - 1) {
-      iteration(P1{}, j, sb, sa, pa, pb);
-      if (j + 1 < NT - 1) {
+    if (NT == 1) {
+      last(P0{}, 0, sa, pb, pa);
+    } else {
+      // iteration 0: softmax_0 with scores_1
+      kcp.copy(Kh, 3 * BC, NK, kst[3]);
+      vcp.copy(Vh, BC, NK, vst[1]);
+      if constexpr (IDLE) {
+        bottom(0.f);
+      } else {
+        const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
+        ws.template scores<1>(sb);
+        constexpr int NS1 = (D / 16) * C::SB;
+        interleave_mfma_valu<NS1, NS1, 2, 4>();
+        bottom(alpha);
+      }
+      // iterations 1 .. NT-2, four per trip so register sets alternate and
+      // every stage index is a constant
+      int j = 1;
+      for (; j + 3 < NT - 1; j += 4) {
+        iteration(P1{}, j, sb, sa, pa, pb);
         iteration(P2{}, j + 1, sa, sb, pb, pa);
-        if (j + 2 < NT - 1) {
-          iteration(P3{}, j + 2, sb, sa, pa, pb);
-          last(P0{}, j + 3, sa, pb, pa);
+        iteration(P3{}, j + 2, sb, sa, pa, pb);
+        iteration(P0{}, j + 3, sa, sb, pb, pa);
+      }
+      if (j < NT - 1) {
+        iteration(P1{}, j, sb, sa, pa, pb);
+        if (j + 1 < NT - 1) {
+          iteration(P2{}, j + 1, sa, sb, pb, pa);
+          if (j + 2 < NT - 1) {
+            iteration(P3{}, j + 2, sb, sa, pa, pb);
+            last(P0{}, j + 3, sa, pb, pa);
+          } else {
+            last(P3{}, j + 2, sb, pa, pb);
+          }
         } else {
-          last(P3{}, j + 2, sb, pa, pb);
+          last(P2{}, j + 1, sa, pb, pa);
         }
       } else {
-        last(P2{}, j + 1, sa, pb, pa);
+        last(P1{}, j, sb, pa, pb);
       }
-    } else {
-      last(P1{}, j, sb, pa, pb);
     }
-  }
+  };
+  if (idle_wave)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 
   // a7: O = acc / l rounded to the input type (or kept fp32 for a partial);
   // LSE = ln2 * (m + log2 l).  Lane half hi holds columns 32*cb + 8*g + 4*hi
@@ -673,7 +701,7 @@ template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
 static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) {
   if constexpr (D == 128) {
     constexpr int64_t BR8 = FusedCfg<D, BC, 8>::BR;
-    if (a.BH * splits * ((a.N + BR8 - 1) / BR8) >= device_cus())
+    if (a.N >= FusedCfg<D, BC, 4>::BR && a.BH * splits * ((a.N + BR8 - 1) / BR8) >= device_cus())
       return launch16_nw<T, D, PARTIAL, BC, 8>(a, splits, out, lse);
   }
   return launch16_nw<T, D, PARTIAL, BC, 4>(a, splits, out, lse);

@@ -46,19 +46,53 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
 
+  // Loads are issued in groups of U partials before any of them is used, so
+  // a call with few rows (one decode row per head) waits for one memory
+  // round trip per group instead of one per partial; the arithmetic runs in
+  // partial order either way.  Slots past the last partial load partial
+  // G - 1 again (no branch around a load) and are left out of the sums.
+  // The first group's values stay in registers between the two passes.
+  constexpr int U = 8;
+  float lp[U];
+  float4 op[U];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t g = g0 + u < G ? g0 + u : G - 1;
+      lp[u] = Lp[g * rows + row];
+      op[u] = *reinterpret_cast<const float4*>(Op + (g * rows + row) * D + 4 * c4);
+    }
+  };
+  load_group(0);
   float ref = -__builtin_inff();
-  for (int g = 0; g < G; ++g) ref = fmaxf(ref, Lp[g * rows + row]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) ref = fmaxf(ref, lp[u]);
+  for (int g0 = U; g0 < G; g0 += U) {
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) l[u] = Lp[static_cast<int64_t>(g0 + u < G ? g0 + u : G - 1) * rows + row];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ref = fmaxf(ref, l[u]);
+  }
   const float base = (ref == -__builtin_inff()) ? 0.f : ref;
   float total = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int g = 0; g < G; ++g) {
-    const float w = expf(Lp[g * rows + row] - base);
-    const float4 o = *reinterpret_cast<const float4*>(Op + (g * rows + row) * D + 4 * c4);
+  auto add = [&](float lse_g, float4 o) {
+    const float w = expf(lse_g - base);
     total += w;
     acc.x = fmaf(w, o.x, acc.x);
     acc.y = fmaf(w, o.y, acc.y);
     acc.z = fmaf(w, o.z, acc.z);
     acc.w = fmaf(w, o.w, acc.w);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < G) add(lp[u], op[u]);
+  for (int g0 = U; g0 < G; g0 += U) {
+    load_group(g0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (g0 + u < G) add(lp[u], op[u]);
   }
   // total >= 1 whenever some block has keys (the reference block weighs 1)
   const float inv = total > 0.f ? 1.f / total : 0.f;
