@@ -95,9 +95,12 @@ EIGHT_WAVE_N = [1, 17, 32, 33, 64, 65, 100, 129, 255, 256, 257]
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_fused_8wave_form_short_and_ragged(dtype, dev):
     # At d = 128 the launch takes workgroups of 8 waves (256 query rows) when
-    # B*H*ceil(N/256) reaches the CU count (256 on MI355X); 256 heads do so at
-    # every length here.  Every element of O and LSE, NaN-filled before the
-    # launch, against the oracle.
+    # N fills at least one 4-wave tile (128 rows) and B*H*ceil(N/256) reaches
+    # the CU count (256 on MI355X): 256 heads do so from N = 129 on, shorter
+    # heads take 4-wave workgroups.  The last query tile leaves waves without
+    # any query row (they only copy and synchronise) at every length here but
+    # 100, 255 and 256: 3 of 4 at N <= 32, 7 of 8 at N = 257.  Every element of O
+    # and LSE, NaN-filled before the launch, against the oracle.
     H = 256
     for N in EIGHT_WAVE_N:
         q, k, v = make_qkv(1, H, N, 128, dtype, seed_base=9000 + N)
