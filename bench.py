@@ -283,7 +283,7 @@ def summarise_trace(trace_dir, index, spec, bench_args, out_dir=None):
         "",
         f"One row per kernel and launch grid (work-items); the fused forward at this "
         f"workload launches {fused_grid_items(spec)} work-items, other grids of the same "
-        f"kernel belong to the split-KV contrast's head share and to the decode leg.",
+        f"kernel belong to the split-KV contrast's head share.",
         "",
         "| kernel | grid | calls | average (ns) | min (ns) | max (ns) | TFLOP/s at 4BHN^2d |",
         "|---|---|---|---|---|---|---|",

@@ -160,6 +160,14 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uin
                : "v"(voff), "s"(rsrc), "{m0}"(lds_byte)
                : "memory");
 }
+// The same copy marked non-temporal, for data that no other workgroup reads
+// again (the caches then keep it for the shortest time).
+__device__ inline void lds_dma16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :
+               : "v"(voff), "s"(rsrc), "{m0}"(lds_byte)
+               : "memory");
+}
 // The same with 4 bytes per lane: 256 consecutive LDS bytes.
 __device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_byte) {
   asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
@@ -184,8 +192,8 @@ __device__ inline uint32_t lds_address(const void* p) {
 // memory into an LDS stage by the NWV waves of a workgroup.  Wave w writes the 1 KiB blocks
 // b = w + NWV*i (i = 0 .. PER_WAVE-1); with this interleave the swizzle of
 // every row a lane copies is the same, and lane offsets differ between
-// blocks only by a constant.
-template <int D, int BC, int SWZ, int NWV = 4>
+// blocks only by a constant.  NT marks the copies non-temporal.
+template <int D, int BC, int SWZ, int NWV = 4, bool NT = false>
 struct TileCopy {
   static constexpr int CH = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_BLK = 64 / CH;     // rows in one 1 KiB block
@@ -214,8 +222,12 @@ struct TileCopy {
     const auto rsrc = buffer_rsrc(head + static_cast<size_t>(k0) * D,
                                   static_cast<uint32_t>(rows) * (D * 2u));
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      lds_dma16(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * (NWV * 1024u));
+    for (int i = 0; i < PER_WAVE; ++i) {
+      if constexpr (NT)
+        lds_dma16_nt(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * (NWV * 1024u));
+      else
+        lds_dma16(rsrc, voff0 + i * (ROW_STEP * D * 2), stage_byte + lds_wave + i * (NWV * 1024u));
+    }
   }
 };
 

@@ -331,9 +331,10 @@ struct WaveState {
 // and writes the normalised partial output in fp32 to Out[(split*BH + bh),
 // q, :] and its log-sum-exp to Lse[(split*BH + bh), q]; the partials are
 // combined by fa_merge_kernel.  Otherwise (one split) it writes O in the
-// input type and the final LSE.
-template <class T, int D, int BC, bool PARTIAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
+// input type and the final LSE.  STREAM marks the K and V copies
+// non-temporal (fa_fwd_16_stream_kernel below).
+template <class T, int D, int BC, bool PARTIAL, int NW, bool STREAM>
+__device__ __forceinline__ void fused16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, void* __restrict__ Out,
     float* __restrict__ Lse, int Nq, int Nk, int BH, int num_qtiles, int num_splits, int num_wg,
@@ -361,8 +362,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
 
   const int NT = (NK + BC - 1) / BC;   // key tiles
   const bool ragged = (NK % BC) != 0;
-  TileCopy<D, BC, kSwzK, C::NW> kcp;
-  TileCopy<D, BC, kSwzV, C::NW> vcp;
+  TileCopy<D, BC, kSwzK, C::NW, STREAM> kcp;
+  TileCopy<D, BC, kSwzV, C::NW, STREAM> vcp;
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
@@ -554,6 +555,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
   }
 }
 
+template <class T, int D, int BC, bool PARTIAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, void* __restrict__ Out,
+    float* __restrict__ Lse, int Nq, int Nk, int BH, int num_qtiles, int num_splits, int num_wg,
+    float scale) {
+  fused16<T, D, BC, PARTIAL, NW, false>(Q, K, V, Out, Lse, Nq, Nk, BH, num_qtiles, num_splits,
+                                        num_wg, scale);
+}
+
+// Queries shorter than one 4-wave tile (decode): each (head, key range) has
+// a single workgroup, so every K and V byte is read by one workgroup only
+// and the copies are marked non-temporal.  Measured with K and V read from
+// HBM at B8 H32 Nq1 Nk8192: 161 against 182 us; B1 H32 Nq1 Nk16384 (G = 8):
+// 46 against 50 us.  The same copies in the kernel above, whose K and V
+// tiles other query tiles read again from L2, measured up to 1.6% slower at
+// B1 H32 N16384.
+template <class T, int D, int BC, bool PARTIAL>
+__global__ __launch_bounds__(256, 2) void fa_fwd_16_stream_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, void* __restrict__ Out,
+    float* __restrict__ Lse, int Nq, int Nk, int BH, int num_qtiles, int num_splits, int num_wg,
+    float scale) {
+  fused16<T, D, BC, PARTIAL, 4, true>(Q, K, V, Out, Lse, Nq, Nk, BH, num_qtiles, num_splits,
+                                      num_wg, scale);
+}
+
 // ---------------------------------------------------------------- fp32 path
 //
 // fp32 inputs keep every product and sum in fp32 on the vector ALUs (on
@@ -699,9 +727,19 @@ static hipError_t launch16_nw(const FwdArgs& a, int splits, void* out, float* ls
 
 template <class T, int D, bool PARTIAL, int BC = kFusedBC<D>>
 static hipError_t launch16(const FwdArgs& a, int splits, void* out, float* lse) {
+  constexpr int64_t BR4 = FusedCfg<D, BC, 4>::BR;
+  if (a.N < BR4) {
+    const int64_t wg = a.BH * splits;   // one query tile per head and split
+    hipLaunchKernelGGL((fa_fwd_16_stream_kernel<T, D, BC, PARTIAL>), dim3(static_cast<unsigned>(wg)),
+                       dim3(256), 0, a.stream, static_cast<const uint16_t*>(a.Q),
+                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.V), out, lse,
+                       static_cast<int>(a.N), static_cast<int>(a.Nk), static_cast<int>(a.BH), 1,
+                       splits, static_cast<int>(wg), a.scale);
+    return hipGetLastError();
+  }
   if constexpr (D == 128) {
     constexpr int64_t BR8 = FusedCfg<D, BC, 8>::BR;
-    if (a.N >= FusedCfg<D, BC, 4>::BR && a.BH * splits * ((a.N + BR8 - 1) / BR8) >= device_cus())
+    if (a.BH * splits * ((a.N + BR8 - 1) / BR8) >= device_cus())
       return launch16_nw<T, D, PARTIAL, BC, 8>(a, splits, out, lse);
   }
   return launch16_nw<T, D, PARTIAL, BC, 4>(a, splits, out, lse);
