@@ -189,7 +189,8 @@ def test_deterministic(dev):
     assert torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dtype,N,d", [("bf16", 8191, 128), ("fp16", 129, 64), ("fp32", 100, 128)])
+@pytest.mark.parametrize("dtype,N,d", [("bf16", 8191, 128), ("fp16", 129, 64), ("bf16", 77, 128),
+                                         ("fp32", 100, 128)])
 def test_no_writes_outside_outputs(dtype, N, d, dev):
     B, H = 1, 2
     q, k, v = (t.to(dev) for t in make_qkv(B, H, N, d, dtype, seed_base=5))
