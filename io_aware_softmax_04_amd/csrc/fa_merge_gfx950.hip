@@ -35,7 +35,7 @@ __device__ inline void store4(void* O, size_t off, float4 v) {
   }
 }
 
-template <int KIND, int D>
+template <int KIND, int D, int U>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ Op,
                                                        const float* __restrict__ Lp, int G,
                                                        int64_t rows, void* __restrict__ O,
@@ -46,13 +46,13 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
 
-  // Loads are issued in groups of U partials before any of them is used, so
-  // a call with few rows (one decode row per head) waits for one memory
-  // round trip per group instead of one per partial; the arithmetic runs in
-  // partial order either way.  Slots past the last partial load partial
-  // G - 1 again (no branch around a load) and are left out of the sums.
-  // The first group's values stay in registers between the two passes.
-  constexpr int U = 8;
+  // Loads are issued in groups of U partials (the smallest power of two
+  // covering G, at most 8) before any of them is used, so a call with few
+  // rows (one decode row per head) waits for one memory round trip per group
+  // instead of one per partial; the arithmetic runs in partial order either
+  // way.  Slots past the last partial load partial G - 1 again (no branch
+  // around a load) and are left out of the sums.  The first group's values
+  // stay in registers between the two passes.
   float lp[U];
   float4 op[U];
   auto load_group = [&](int g0) {
@@ -101,13 +101,21 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   if (c4 == 0) LSE[row] = total > 0.f ? base + logf(total) : -__builtin_inff();
 }
 
-template <int KIND, int D>
-hipError_t launch_merge_t(const MergeArgs& a) {
+template <int KIND, int D, int U>
+hipError_t launch_merge_u(const MergeArgs& a) {
   constexpr int RPB = 256 / (D / 4);
   const int64_t wg = (a.rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((fa_merge_kernel<KIND, D>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
+  hipLaunchKernelGGL((fa_merge_kernel<KIND, D, U>), dim3(static_cast<unsigned>(wg)), dim3(256), 0,
                      a.stream, a.O_part, a.LSE_part, a.G, a.rows, a.O, a.LSE);
   return hipGetLastError();
+}
+
+template <int KIND, int D>
+hipError_t launch_merge_t(const MergeArgs& a) {
+  if (a.G <= 1) return launch_merge_u<KIND, D, 1>(a);
+  if (a.G == 2) return launch_merge_u<KIND, D, 2>(a);
+  if (a.G <= 4) return launch_merge_u<KIND, D, 4>(a);
+  return launch_merge_u<KIND, D, 8>(a);
 }
 
 }  // namespace
