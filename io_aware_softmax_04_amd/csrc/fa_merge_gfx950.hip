@@ -47,12 +47,13 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   if (row >= rows) return;
 
   // Loads are issued in groups of U partials (the smallest power of two
-  // covering G, at most 8) before any of them is used, so a call with few
+  // covering G, 16 for G > 8) before any of them is used, so a call with few
   // rows (one decode row per head) waits for one memory round trip per group
   // instead of one per partial; the arithmetic runs in partial order either
   // way.  Slots past the last partial load partial G - 1 again (no branch
   // around a load) and are left out of the sums.  The first group's values
-  // stay in registers between the two passes.
+  // stay in registers between the two passes; past it the maximum reads the
+  // LSEs LC at a time.
   float lp[U];
   float4 op[U];
   auto load_group = [&](int g0) {
@@ -67,12 +68,13 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   float ref = -__builtin_inff();
 #pragma unroll
   for (int u = 0; u < U; ++u) ref = fmaxf(ref, lp[u]);
-  for (int g0 = U; g0 < G; g0 += U) {
-    float l[U];
+  constexpr int LC = U > 8 ? 32 : U;
+  for (int g0 = U; g0 < G; g0 += LC) {
+    float l[LC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) l[u] = Lp[static_cast<int64_t>(g0 + u < G ? g0 + u : G - 1) * rows + row];
+    for (int u = 0; u < LC; ++u) l[u] = Lp[static_cast<int64_t>(g0 + u < G ? g0 + u : G - 1) * rows + row];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ref = fmaxf(ref, l[u]);
+    for (int u = 0; u < LC; ++u) ref = fmaxf(ref, l[u]);
   }
   const float base = (ref == -__builtin_inff()) ? 0.f : ref;
   float total = 0.f;
@@ -115,7 +117,8 @@ hipError_t launch_merge_t(const MergeArgs& a) {
   if (a.G <= 1) return launch_merge_u<KIND, D, 1>(a);
   if (a.G == 2) return launch_merge_u<KIND, D, 2>(a);
   if (a.G <= 4) return launch_merge_u<KIND, D, 4>(a);
-  return launch_merge_u<KIND, D, 8>(a);
+  if (a.G <= 8) return launch_merge_u<KIND, D, 8>(a);
+  return launch_merge_u<KIND, D, 16>(a);
 }
 
 }  // namespace

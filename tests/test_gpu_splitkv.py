@@ -173,7 +173,10 @@ def test_splitkv_qk_with_equal_lengths_is_splitkv(dev):
 @pytest.mark.parametrize("d", [64, 128])
 def test_merge_entry_point(out_dtype, d, dev):
     rng = np.random.default_rng(d)
-    for G, rows in ((1, 5), (2, 333), (7, 1000)):
+    # G covers every load-group size of the kernel (1, 2, 4, 8 and 16 with
+    # several groups and LSE chunks)
+    for G, rows in ((1, 5), (2, 333), (3, 64), (4, 100), (7, 1000), (9, 77), (33, 40),
+                    (100, 20)):
         o_part = rng.standard_normal((G, rows, d)).astype(np.float32)
         lse_part = rng.uniform(-20, 20, (G, rows)).astype(np.float32)
         if G > 1:
