@@ -71,8 +71,8 @@ constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kTargetWaves = 2048;   // 8 per CU on 256 CUs
 // With fewer query rows than one query tile (decode) every workgroup is
 // bound by its stream of keys and values: one 4-wave workgroup per CU
-// measured fastest (B1 H8 Nq1 Nk32768: 32 us against 37 us at 2048 waves;
-// B1 H32 Nq1 Nk16384: 46 against 48 us; K and V not in the last-level
+// measured fastest (B1 H8 Nq1 Nk32768: 29 us against 35 us at 2048 waves;
+// B1 H32 Nq1 Nk16384: 44.5 against 44.6 us; K and V not in the last-level
 // cache).
 constexpr int64_t kTargetWavesShortQueries = 1024;
 constexpr int64_t kMinTilesPerSplit = 16;

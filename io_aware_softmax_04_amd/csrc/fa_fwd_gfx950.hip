@@ -367,11 +367,32 @@ __device__ __forceinline__ void fused16(
   kcp.init(wave, lane);
   vcp.init(wave, lane);
 
-  // a2 prologue: K_0, K_1, K_2 and V_0 in flight while Q is loaded
+  // K is copied 3 tiles ahead of its scores, V VA tiles ahead of its P V
+  // product.  The tile kernel waits for every copy at each barrier (after odd
+  // iterations); the stream form (short query blocks, bound by the stream of
+  // K and V) synchronises after every iteration and keeps its newest KEEP
+  // tile copies in flight across each wait, V being copied two ahead so the
+  // ring still has the stage (a host model of both schedules checks every
+  // stage's copy, wait, barrier and read order).
+  constexpr int VA = STREAM ? 2 : 1;
+  constexpr int KEEP = STREAM ? 3 : 0;
+  auto wait_copies = [&](auto keep_c) {
+    constexpr int n = decltype(keep_c)::value * decltype(kcp)::PER_WAVE;   // instructions
+    static_assert(n < 64, "vmcnt holds 6 bits");
+    // vmcnt(n) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(0): the LDS reads
+    // are done as well
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+  };
+  using Keep0 = std::integral_constant<int, 0>;
+  using KeepN = std::integral_constant<int, KEEP>;
+
+  // a2 prologue: K_0, K_1, K_2 and V_0 (.. V_{VA-1}) in flight while Q is
+  // loaded
   kcp.copy(Kh, 0, NK, kst[0]);
   kcp.copy(Kh, BC, NK, kst[1]);
   kcp.copy(Kh, 2 * BC, NK, kst[2]);
   vcp.copy(Vh, 0, NK, vst[0]);
+  if constexpr (VA == 2) vcp.copy(Vh, BC, NK, vst[1]);
 
   // a1: this lane's query row, its Q fragments, the running state.  A
   // negative scale is folded into Q (negation is exact) so the scale applied
@@ -413,9 +434,13 @@ __device__ __forceinline__ void fused16(
     // ahead for the whole tile (1.1-1.4% faster at B2 H16 N4096 and B2 H8
     // N8191 than 6 ahead with the lead draining over the tile); 8 at d = 64
     constexpr int LEAD = D == 128 ? 4 : 8;
-    auto bottom = [&](float alpha) {
+    // keep_c: tile copies left in flight by the wait (0 in the last iteration)
+    auto bottom = [&](float alpha, auto keep_c) {
       if constexpr (!IDLE) ws.rescale(alpha);
-      __builtin_amdgcn_s_waitcnt(0);
+      if constexpr (decltype(keep_c)::value == 0)
+        __builtin_amdgcn_s_waitcnt(0);
+      else
+        wait_copies(keep_c);
       __syncthreads();
     };
     // one full iteration j with parity P (compile-time)
@@ -424,14 +449,14 @@ __device__ __forceinline__ void fused16(
       constexpr int P = decltype(par)::value;   // j % 4
       if constexpr (IDLE) {
         kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
-        vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
+        vcp.copy(Vh, (j + VA) * BC, NK, vst[(P + VA) % 4]);
       } else {
         // raised issue priority from the copies through the products; dropped
         // again before the wait and barrier (measured 0.8% faster at d = 128,
         // 3.8% at d = 64, bit-identical output)
         __builtin_amdgcn_s_setprio(1);
         kcp.copy(Kh, (j + 3) * BC, NK, kst[(P + 3) % 4]);
-        vcp.copy(Vh, (j + 1) * BC, NK, vst[(P + 1) % 4]);
+        vcp.copy(Vh, (j + VA) * BC, NK, vst[(P + VA) % 4]);
         const float rs = ws.softmax_lazy(s_cur, p_cur, c2);
         ws.template pv_scores<(P + 3) % 4, (P + 1) % 4>(p_prev, s_nxt);
         // d = 128 keeps its reads LEAD ahead for the whole tile, with three
@@ -449,7 +474,10 @@ __device__ __forceinline__ void fused16(
         if (ws.commit_lazy(rs, s_cur, p_cur, c2, alpha)) ws.rescale(alpha);
         __builtin_amdgcn_s_setprio(0);
       }
-      if constexpr (P % 2 == 1) {
+      if constexpr (STREAM) {
+        wait_copies(KeepN{});
+        __syncthreads();
+      } else if constexpr (P % 2 == 1) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -459,12 +487,12 @@ __device__ __forceinline__ void fused16(
                     vec8 (&p_cur)[C::KSTEPS]) {
       constexpr int P = decltype(par)::value;   // j % 4
       if constexpr (IDLE) {
-        bottom(0.f);
+        bottom(0.f, Keep0{});
       } else {
         const float alpha = ragged ? ws.template softmax<true>(s_cur, p_cur, c2, NK - j * BC)
                                    : ws.template softmax<false>(s_cur, p_cur, c2, BC);
         if (j > 0) ws.template pv<(P + 3) % 4>(p_prev);
-        bottom(alpha);
+        bottom(alpha, Keep0{});
         ws.template pv<P>(p_cur);
       }
     };
@@ -478,15 +506,15 @@ __device__ __forceinline__ void fused16(
     } else {
       // iteration 0: softmax_0 with scores_1
       kcp.copy(Kh, 3 * BC, NK, kst[3]);
-      vcp.copy(Vh, BC, NK, vst[1]);
+      vcp.copy(Vh, VA * BC, NK, vst[VA]);
       if constexpr (IDLE) {
-        bottom(0.f);
+        bottom(0.f, KeepN{});
       } else {
         const float alpha = ws.template softmax<false>(sa, pa, c2, BC);
         ws.template scores<1>(sb);
         constexpr int NS1 = (D / 16) * C::SB;
         interleave_mfma_valu<NS1, NS1, 2, 4>();
-        bottom(alpha);
+        bottom(alpha, KeepN{});
       }
       // iterations 1 .. NT-2, four per trip so register sets alternate and
       // every stage index is a constant
@@ -567,11 +595,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fa_fwd_16_kernel(
 
 // Queries shorter than one 4-wave tile (decode): each (head, key range) has
 // a single workgroup, so every K and V byte is read by one workgroup only
-// and the copies are marked non-temporal.  Measured with K and V read from
-// HBM at B8 H32 Nq1 Nk8192: 161 against 182 us; B1 H32 Nq1 Nk16384 (G = 8):
-// 46 against 50 us.  The same copies in the kernel above, whose K and V
-// tiles other query tiles read again from L2, measured up to 1.6% slower at
-// B1 H32 N16384.
+// and the workgroup is bound by that stream.  The copies are marked
+// non-temporal (with K and V read from HBM, B8 H32 Nq1 Nk8192: 161 against
+// 182 us; the same marking in the kernel above, whose K and V tiles other
+// query tiles read again from L2, measured up to 1.6% slower at B1 H32
+// N16384), and the schedule keeps three tile copies in flight across its
+// barriers instead of draining them every two tiles (153 against 161 us;
+// B2 H16 Nq1 Nk4096: 16.0 against 18.0 us with the merge).
 template <class T, int D, int BC, bool PARTIAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16_stream_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
