@@ -331,8 +331,11 @@ struct WaveState {
 // and writes the normalised partial output in fp32 to Out[(split*BH + bh),
 // q, :] and its log-sum-exp to Lse[(split*BH + bh), q]; the partials are
 // combined by fa_merge_kernel.  Otherwise (one split) it writes O in the
-// input type and the final LSE.  STREAM marks the K and V copies
-// non-temporal (fa_fwd_16_stream_kernel below).
+// input type and the final LSE.  STREAM (fa_fwd_16_stream_kernel below)
+// marks the K and V copies non-temporal and changes the schedule above: V
+// copied in iteration t-2, a wait and barrier after every iteration that
+// leaves the three newest tile copies in flight, and a full wait only in the
+// last iteration.
 template <class T, int D, int BC, bool PARTIAL, int NW, bool STREAM>
 __device__ __forceinline__ void fused16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
