@@ -223,7 +223,9 @@ size_t fa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, in
  *   num_splits  as fa_fwd_splitkv, except that with fewer than 128 query
  *               rows per head (one query tile: decode) the automatic G aims
  *               at about 1024 waves, one 4-wave workgroup per CU, since each
- *               workgroup is then bound by its stream of keys and values.
+ *               workgroup is then bound by its stream of keys and values;
+ *               each key range then keeps at least 128 keys, and more than
+ *               16 ranges are taken only while each keeps 512.
  *   Nq = 0 (or B = 0 or H = 0) is an empty call; Nq > 0 with Nk = 0 is
  *   FA_ERR_SHAPE (a softmax over no keys is undefined).  Both lengths obey
  *   the limits of fa_fwd.  fa_fwd_splitkv(..., N, ...) is this call with

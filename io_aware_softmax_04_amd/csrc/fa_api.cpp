@@ -76,6 +76,17 @@ constexpr int64_t kTargetWaves = 2048;   // 8 per CU on 256 CUs
 // cache).
 constexpr int64_t kTargetWavesShortQueries = 1024;
 constexpr int64_t kMinTilesPerSplit = 16;
+// With short queries a range keeps at least kMinKeysShortQueries keys (the
+// workgroup's fixed cost against its stream), and more than
+// kManySplitsShortQueries ranges only when each keeps kMinKeysManySplits
+// (the merge of many partials costs more than the extra workgroups win on
+// short ranges).  Measured with K and V read from HBM (bf16, us): B2 H16 Nq1
+// Nk1024 d128 G = 8: 9.0 against 12.1 at the 16-tile floor; B1 H8 Nq1 Nk4096
+// d64 G = 16: 9.0 against 13.7 at that floor and 11.1 at G = 32; B1 H8 Nq1
+// Nk32768 d128 keeps G = 32.
+constexpr int64_t kMinKeysShortQueries = 128;
+constexpr int64_t kManySplitsShortQueries = 16;
+constexpr int64_t kMinKeysManySplits = 512;
 constexpr int kMaxMergeParts = 4096;
 
 struct Region {
@@ -204,11 +215,17 @@ int fa_splitkv_qk_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
   if (g <= 0) {
     // enough waves for one full round of the chip
     const int64_t per_split = iofa::fused_waves(dtype, B * H, Nq, 1);
-    const int64_t target = Nq < iofa::fused_query_tile(dtype) ? kTargetWavesShortQueries
-                                                              : kTargetWaves;
-    g = (target + per_split - 1) / per_split;
-    const int64_t longest = tiles / kMinTilesPerSplit;
-    if (g > longest) g = longest;
+    if (Nq < iofa::fused_query_tile(dtype)) {
+      g = (kTargetWavesShortQueries + per_split - 1) / per_split;
+      const int64_t longest = Nk / kMinKeysShortQueries;
+      if (g > longest) g = longest;
+      const int64_t many = std::max(kManySplitsShortQueries, Nk / kMinKeysManySplits);
+      if (g > many) g = many;
+    } else {
+      g = (kTargetWaves + per_split - 1) / per_split;
+      const int64_t longest = tiles / kMinTilesPerSplit;
+      if (g > longest) g = longest;
+    }
   }
   if (g > cap) g = cap;
   if (g < 1) g = 1;

@@ -209,15 +209,25 @@ def test_split_count_policy_for_queries_and_keys_of_different_lengths(lib):
     for B, H, N, d in ((2, 2, 4096, 128), (2, 16, 4096, 128), (4, 2, 1024, 128), (1, 1, 300, 64)):
         assert (iofa.fa_splitkv_qk_num_splits(B, H, N, N, d, 2, 0)
                 == iofa.fa_splitkv_num_splits(B, H, N, d, 2, 0))
-    # decode at B2 H16: one 4-wave query tile per head (128 waves), so 16
-    # ranges would reach 2048 waves; 128 key tiles allow 8 of at least 16
+    # fewer query rows than one tile (decode): about 1024 waves, one 4-wave
+    # workgroup per CU; at B2 H16 one query tile per head gives 128 waves, so
+    # 8 ranges
     assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 4096, 128, 2, 0) == 8
-    # one head decoding 16384 keys: 512 key tiles, 32 ranges of 16
-    assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 16384, 128, 2, 0) == 32
-    # fewer query rows than one tile: about 1024 waves (one 4-wave workgroup
-    # per CU), so 8 heads of one row take 32 ranges, not 64
+    # 8 heads of one row take 32 ranges, not 64; 32 heads take 8
     assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 32768, 128, 2, 0) == 32
     assert iofa.fa_splitkv_qk_num_splits(1, 32, 1, 16384, 128, 2, 0) == 8
+    # each range keeps at least 128 keys: 1024 keys allow 8, 512 allow 4
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 1024, 128, 2, 0) == 8
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 512, 128, 2, 0) == 4
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 1, 512, 64, 2, 0) == 4
+    assert iofa.fa_splitkv_qk_num_splits(8, 32, 1, 100, 128, 2, 0) == 1
+    # more than 16 ranges only while each keeps 512 keys: one head decoding
+    # 16384 keys takes 32 ranges, 8 heads of 4096 keys 16 (not 32)
+    assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 16384, 128, 2, 0) == 32
+    assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 4096, 128, 2, 0) == 16
+    assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 4096, 64, 2, 0) == 16
+    # a full query tile keeps the 2048-wave target and the 16-tile floor
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 128, 1024, 128, 2, 0) == 2
     # the cap follows the key tiles, not the query rows
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 5000, 100, 128, 2, 99) == 4
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 0, 128, 2, 0) == 0     # no keys
