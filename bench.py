@@ -76,6 +76,9 @@ def parse():
                    help="kernel the counter summary covers")
     p.add_argument("--copy-mib", type=int, default=1024,
                    help="size of the calibration copy in those runs")
+    p.add_argument("--sweep-splits", action="store_true",
+                   help="time the split-KV forward at every split count of the sweep lists "
+                        "and write the tables to " + SWEEP_FILE + ", then exit")
     return p.parse_args()
 
 
@@ -775,6 +778,84 @@ def decode_measure(spec, torch, iofa, dev):
     }
 
 
+# Shapes (B, H, Nq, Nk, d) and split counts of the split-count sweep
+SWEEP_FULL = [(2, 2, 4096, 4096, 128), (1, 1, 16384, 16384, 128), (2, 4, 2048, 2048, 128),
+              (1, 4, 8192, 8192, 128), (4, 2, 1024, 1024, 128)]
+SWEEP_FULL_G = [1, 2, 3, 4, 6, 8, 12, 16]
+SWEEP_DECODE = [(2, 16, 1, 4096, 128), (2, 16, 4, 4096, 128), (2, 16, 64, 4096, 128),
+                (1, 32, 1, 16384, 128), (8, 32, 1, 8192, 128), (8, 32, 1, 1024, 128),
+                (1, 8, 1, 32768, 128), (2, 16, 1, 1024, 128), (2, 16, 1, 512, 128),
+                (1, 8, 1, 4096, 128), (1, 8, 1, 1024, 128), (1, 32, 1, 2048, 128),
+                (2, 16, 1, 4096, 64), (2, 16, 1, 512, 64), (1, 8, 1, 4096, 64),
+                (1, 8, 1, 1024, 64), (1, 32, 1, 2048, 64), (4, 32, 1, 2048, 64)]
+SWEEP_DECODE_G = [1, 2, 4, 8, 16, 32, 64]
+SWEEP_FILE = "profiles/splitkv_sweep_bf16.md"
+
+
+def sweep_splits(torch, iofa, dev):
+    """Time fa_fwd_splitkv_qk at every split count of the sweep lists (bf16,
+    graphs of 20 calls rotating over copies of K and V that hold at least
+    DECODE_ROTATION_BYTES) and write the tables, with the split count the
+    library picks, to SWEEP_FILE."""
+    from workloads import make_qkv
+
+    def table(shapes, gs, title):
+        rows = [f"## {title}", "",
+                "| B H Nq Nk d | " + " | ".join(f"G={g}" for g in gs) + " | policy |",
+                "|---" * (len(gs) + 2) + "|"]
+        for (B, H, Nq, Nk, d) in shapes:
+            q = make_qkv(B, H, Nq, d, "bf16", seed_base=7001)[0].to(dev)
+            _, k, v = (t.to(dev) for t in make_qkv(B, H, Nk, d, "bf16", seed_base=7002))
+            kv_bytes = 2 * k.numel() * k.element_size()
+            copies = max(1, -(-DECODE_ROTATION_BYTES // kv_bytes))
+            kvs = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+            scale = iofa.default_scale(d)
+            times = {}
+            auto = iofa.fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, q.dtype, 0)
+            for g in gs + [auto]:
+                gg = iofa.fa_splitkv_qk_num_splits(B, H, Nq, Nk, d, q.dtype, g)
+                if gg in times:           # capped at the key-tile count, or timed
+                    continue
+                nbytes = iofa.fa_splitkv_qk_workspace_bytes(B, H, Nq, Nk, d, q.dtype, gg)
+                ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+                turn = [0]
+
+                def call(gg=gg, ws=ws, turn=turn):
+                    kc, vc = kvs[turn[0] % copies]
+                    turn[0] += 1
+                    iofa.fa_fwd_splitkv_qk(q, kc, vc, o, lse, ws, scale, gg)
+
+                times[gg] = time_graph(call, torch) * 1e3
+            best = min(times.values())
+            cells = [("—" if g not in times else
+                      (f"**{times[g]:.1f}**" if times[g] <= best * 1.005 else f"{times[g]:.1f}"))
+                     for g in gs]
+            rows.append(f"| {B} {H} {Nq} {Nk} {d} | " + " | ".join(cells) +
+                        f" | {auto} ({times[auto] / best:.2f}× the fastest) |")
+            print(f"[bench] sweep {B} {H} {Nq} {Nk} {d}: policy G={auto}", file=sys.stderr,
+                  flush=True)
+            del kvs
+        return rows + [""]
+
+    lines = ["# Split-count sweep of the split-KV forward, bf16", "",
+             "Command (one MI355X, from the repository root):", "", "```",
+             "python bench.py --sweep-splits", "```", "",
+             "Microseconds per call of `fa_fwd_splitkv_qk` at each requested split count G: "
+             "20 calls captured in a graph and replayed 10 times between two events, the calls "
+             f"rotating over copies of K and V that together hold at least "
+             f"{DECODE_ROTATION_BYTES >> 20} MiB, so every call reads K and V from HBM. Bold: "
+             "within 0.5% of the fastest. policy: the G the library picks on its own, and its "
+             "time over the fastest. A dash: G above the key-tile count (the call uses fewer).",
+             ""]
+    lines += table(SWEEP_FULL, SWEEP_FULL_G, "Query blocks of at least one tile (Nq = Nk)")
+    lines += table(SWEEP_DECODE, SWEEP_DECODE_G, "Query blocks shorter than one tile (decode)")
+    with open(SWEEP_FILE, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines))
+    print(f"[bench] wrote {SWEEP_FILE}", file=sys.stderr, flush=True)
+
+
 def backward_measure(q, k, v, scale, spec, args, torch, iofa, dev):
     """The backward pass on the same workload.  TFLOP/s on the algorithmic
     count 10*B*H*N^2*d (the five N^2 d products a single pass needs, 2.5x the
@@ -922,6 +1003,9 @@ def main():
     iofa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep_splits:
+        sweep_splits(torch, iofa, dev)
+        return
 
     q, k, v, scale, spec = workload_qkv(args.workload)
     B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]

@@ -64,9 +64,10 @@ bool within_limits(int64_t B, int64_t H, int64_t N, int64_t d) {
 
 // Split-KV policy: at most this many key ranges, and enough of them that the
 // partial pass has about this many waves (eight per CU on 256 CUs), but,
-// when G is chosen automatically, no fewer than kMinTilesPerSplit key tiles
-// per range (shorter ranges spend more on the pipeline's fill and drain and on
-// the merge than the extra workgroups win back).
+// when G is chosen automatically, no fewer than kMinKeysPerSplit keys per
+// range (shorter ranges spend more on the pipeline's fill and drain and on
+// the merge than the extra workgroups win back: B2 H4 N2048 d128 took 33.3
+// us unsplit, 34.0 at G = 2 and 36.6 at G = 4, with K and V read from HBM).
 constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kTargetWaves = 2048;   // 8 per CU on 256 CUs
 // With fewer query rows than one query tile (decode) every workgroup is
@@ -75,14 +76,14 @@ constexpr int64_t kTargetWaves = 2048;   // 8 per CU on 256 CUs
 // B1 H32 Nq1 Nk16384: 44.5 against 44.6 us; K and V not in the last-level
 // cache).
 constexpr int64_t kTargetWavesShortQueries = 1024;
-constexpr int64_t kMinTilesPerSplit = 16;
+constexpr int64_t kMinKeysPerSplit = 1024;
 // With short queries a range keeps at least kMinKeysShortQueries keys (the
 // workgroup's fixed cost against its stream), and more than
 // kManySplitsShortQueries ranges only when each keeps kMinKeysManySplits
 // (the merge of many partials costs more than the extra workgroups win on
 // short ranges).  Measured with K and V read from HBM (bf16, us): B2 H16 Nq1
-// Nk1024 d128 G = 8: 9.0 against 12.1 at the 16-tile floor; B1 H8 Nq1 Nk4096
-// d64 G = 16: 9.0 against 13.7 at that floor and 11.1 at G = 32; B1 H8 Nq1
+// Nk1024 d128 G = 8: 9.0 against 12.1 at G = 2; B1 H8 Nq1 Nk4096
+// d64 G = 16: 9.0 against 13.7 at G = 4 and 11.1 at G = 32; B1 H8 Nq1
 // Nk32768 d128 keeps G = 32.
 constexpr int64_t kMinKeysShortQueries = 128;
 constexpr int64_t kManySplitsShortQueries = 16;
@@ -223,7 +224,7 @@ int fa_splitkv_qk_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
       if (g > many) g = many;
     } else {
       g = (kTargetWaves + per_split - 1) / per_split;
-      const int64_t longest = tiles / kMinTilesPerSplit;
+      const int64_t longest = Nk / kMinKeysPerSplit;
       if (g > longest) g = longest;
     }
   }

@@ -163,11 +163,13 @@ def test_split_count_policy(lib):
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 128, 2, 99) == 4      # 4 key tiles of 32
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 2, 99) == 2       # 2 key tiles of 64
     assert iofa.fa_splitkv_num_splits(1, 1, 1 << 20, 128, 2, 1000) == 64
-    # automatic G keeps at least 16 key tiles per range: 32 tiles of 32 keys
-    # at N = 1024, d = 128 allow 2 ranges although 64 workgroups ask for 8
-    assert iofa.fa_splitkv_num_splits(4, 2, 1024, 128, 2, 0) == 2
+    # automatic G keeps at least 1024 keys per range: at N = 1024 no split
+    # although 64 workgroups ask for 8, at N = 2048 two ranges
+    assert iofa.fa_splitkv_num_splits(4, 2, 1024, 128, 2, 0) == 1
+    assert iofa.fa_splitkv_num_splits(2, 4, 2048, 128, 2, 0) == 2
+    assert iofa.fa_splitkv_num_splits(2, 4, 2048, 64, 2, 0) == 2
     assert iofa.fa_splitkv_num_splits(4, 2, 1024, 128, 2, 8) == 8      # an explicit G stays
-    assert iofa.fa_splitkv_num_splits(1, 1, 300, 128, 2, 0) == 1       # 10 tiles: no split
+    assert iofa.fa_splitkv_num_splits(1, 1, 300, 128, 2, 0) == 1       # 300 keys: no split
     assert iofa.fa_splitkv_num_splits(1, 1, 16384, 128, 2, 0) == 4
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 96, 2, 0) == 0        # invalid d
     assert iofa.fa_splitkv_num_splits(1, 1, 100, 64, 5, 0) == 0        # invalid dtype
@@ -226,8 +228,9 @@ def test_split_count_policy_for_queries_and_keys_of_different_lengths(lib):
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 16384, 128, 2, 0) == 32
     assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 4096, 128, 2, 0) == 16
     assert iofa.fa_splitkv_qk_num_splits(1, 8, 1, 4096, 64, 2, 0) == 16
-    # a full query tile keeps the 2048-wave target and the 16-tile floor
-    assert iofa.fa_splitkv_qk_num_splits(2, 16, 128, 1024, 128, 2, 0) == 2
+    # a full query tile keeps the 2048-wave target and the 1024-key floor
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 128, 1024, 128, 2, 0) == 1
+    assert iofa.fa_splitkv_qk_num_splits(2, 16, 128, 4096, 128, 2, 0) == 4
     # the cap follows the key tiles, not the query rows
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 5000, 100, 128, 2, 99) == 4
     assert iofa.fa_splitkv_qk_num_splits(1, 1, 1, 0, 128, 2, 0) == 0     # no keys
