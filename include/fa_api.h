@@ -162,8 +162,8 @@ int fa_naive_fwd(const void* Q, const void* K, const void* V, void* O,
  * O = sum_g e^{LSE_g - LSE} O_g.
  *
  *   num_splits  G requested; 0 (or less) chooses G so that pass 1 has about
- *               2048 waves (eight per CU) while every range keeps at least 16
- *               key tiles; G is clamped to [1, min(64, key tiles)].
+ *               2048 waves (eight per CU) while every range keeps at least
+ *               1024 keys; G is clamped to [1, min(64, key tiles)].
  *               With G = 1 the call is fa_fwd and the workspace is unused.
  *   workspace   caller-owned device memory of at least
  *               fa_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits)
